@@ -1,0 +1,27 @@
+"""TwELL sparse gated-FFN forward on MI355X (gfx950).
+
+The computation lives in libtwell.so (hand-written HIP kernels behind the C ABI
+declared in include/twell.h). This package is its thin Python binding: it
+passes device pointers of torch tensors and the current stream, nothing more.
+"""
+
+from ._lib import (  # noqa: F401
+    OP_DENSE_FALLBACK,
+    OP_DENSE_FFN,
+    OP_FFN_FORWARD,
+    OP_GATE_PACK,
+    LIB_PATH,
+    Packed,
+    TwellError,
+    Workspace,
+    dense_fallback,
+    dense_ffn_forward,
+    ffn_forward,
+    fused_updown,
+    gate_pack,
+    header_functions,
+    lib,
+    packed_view,
+    status_string,
+    workspace_bytes,
+)

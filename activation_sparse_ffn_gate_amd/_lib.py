@@ -1,0 +1,284 @@
+"""ctypes binding of libtwell.so — argument marshalling only.
+
+Every step of the forward runs in the library's HIP kernels; this module only
+checks tensor shapes/dtypes/devices, passes raw device pointers and the current
+HIP stream, and turns status codes into exceptions. It never computes a
+result itself and has no fallback: if libtwell.so is missing it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libtwell.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "twell.h")
+
+TWELL_OK = 0
+OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK = 0, 1, 2, 3
+
+
+class TwellError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Packed(ctypes.Structure):
+    _fields_ = [
+        ("vals", ctypes.c_void_p),
+        ("idx", ctypes.c_void_p),
+        ("counts", ctypes.c_void_p),
+        ("ovf_rows", ctypes.c_void_p),
+        ("n_ovf", ctypes.c_void_p),
+    ]
+
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_PK = ctypes.POINTER(_Packed)
+_SIGNATURES = {
+    "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
+    "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
+    "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "twell_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32]),
+    "twell_packed_view": (ctypes.c_int, [_P, _SZ, _I64, _I64, _I64, _I32, _I32, _PK]),
+    "twell_status_string": (ctypes.c_char_p, [_I32]),
+    "twell_abi_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtwell.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m activation_sparse_ffn_gate_amd._build` "
+                "(there is no CPU fallback)"
+            )
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/twell.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(twell_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().twell_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != TWELL_OK:
+        raise TwellError(status, where)
+
+
+def workspace_bytes(op: int, M: int, d: int, F: int, T: int = 0, C: int = 0) -> int:
+    return int(lib().twell_workspace_bytes(op, M, d, F, T, C))
+
+
+# --------------------------------------------------------------- torch-facing API
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16(t, name, shape):
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bf16 (or its 16-bit bit pattern), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _ptr(t)
+
+
+def _f32_out(t, name, shape, device):
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 of shape {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    return t
+
+
+@dataclass
+class Packed:
+    """Device tensors of one TwELL packing (see twell_packed in include/twell.h)."""
+
+    vals: "object"  # float32 [M, F/T, C]
+    idx: "object"  # uint8   [M, F/T, C]
+    counts: "object"  # int16 storage of uint16 [M, F/T]
+    ovf_rows: "object"  # int32 [M]
+    n_ovf: "object"  # int32 [1]
+    T: int
+    C: int
+
+    @classmethod
+    def empty(cls, M, F, T, C, device):
+        torch = _torch()
+        nT = F // T
+        return cls(
+            torch.empty((M, nT, C), dtype=torch.float32, device=device),
+            torch.empty((M, nT, C), dtype=torch.uint8, device=device),
+            torch.empty((M, nT), dtype=torch.int16, device=device),
+            torch.empty((max(M, 1),), dtype=torch.int32, device=device),
+            torch.empty((1,), dtype=torch.int32, device=device),
+            T,
+            C,
+        )
+
+    def _c(self) -> _Packed:
+        return _Packed(self.vals.data_ptr(), self.idx.data_ptr(), self.counts.data_ptr(),
+                       self.ovf_rows.data_ptr(), self.n_ovf.data_ptr())
+
+
+class Workspace:
+    """Zero-filled, 256-byte aligned device scratch, grown on demand and reused.
+
+    The library leaves the control block zeroed after each call, so the buffer
+    is zero-filled only when it is (re)allocated.
+    """
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256) + 256, dtype=torch.uint8, device=self.device)
+        base = self.buf.data_ptr()
+        off = (-base) % 256
+        return ctypes.c_void_p(base + off), self.buf.numel() - off
+
+
+_WS: dict = {}
+
+
+def _workspace(ws, device):
+    if ws is None:
+        key = (device.type, device.index)
+        if key not in _WS:
+            _WS[key] = Workspace(device)
+        ws = _WS[key]
+    return ws
+
+
+def gate_pack(x, Wg, T: int, C: int, out: Packed | None = None, z_debug=None, workspace=None) -> Packed:
+    """twell_gate_pack. z_debug: None, or a float32 [M, F] tensor to receive z."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    px, pw = _bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d))
+    out = out or Packed.empty(M, F, T, C, x.device)
+    pz = ctypes.c_void_p(0)
+    if z_debug is not None:
+        _f32_out(z_debug, "z_debug", (M, F), x.device)
+        pz = _ptr(z_debug)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_GATE_PACK, M, d, F, T, C))
+    pk = out._c()
+    _check(lib().twell_gate_pack(px, pw, M, d, F, T, C, ctypes.byref(pk), pz, wp, wn, _stream(x)), "twell_gate_pack")
+    return out
+
+
+def fused_updown(x, WuT, Wd, packed: Packed, y=None):
+    M, d = x.shape
+    F = WuT.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    pk = packed._c()
+    _check(lib().twell_fused_updown(*args, ctypes.byref(pk), M, d, F, packed.T, packed.C, _ptr(y), _stream(x)),
+           "twell_fused_updown")
+    return y
+
+
+def dense_fallback(x, Wg, WuT, Wd, packed: Packed, y, workspace=None):
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_DENSE_FALLBACK, M, d, F))
+    pk = packed._c()
+    _check(lib().twell_dense_fallback(*args, ctypes.byref(pk), M, d, F, _ptr(y), wp, wn, _stream(x)),
+           "twell_dense_fallback")
+    return y
+
+
+def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None):
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_FFN_FORWARD, M, d, F, T, C))
+    _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _ptr(y), wp, wn, _stream(x)), "twell_ffn_forward")
+    return y
+
+
+def dense_ffn_forward(x, Wg, WuT, Wd, y=None, workspace=None):
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_DENSE_FFN, M, d, F))
+    _check(lib().twell_dense_ffn_forward(*args, M, d, F, _ptr(y), wp, wn, _stream(x)), "twell_dense_ffn_forward")
+    return y
+
+
+def packed_view(M: int, d: int, F: int, T: int, C: int, workspace=None, device=None) -> Packed:
+    """Tensor views of the packing twell_ffn_forward keeps in the workspace."""
+    torch = _torch()
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    ws = _workspace(workspace, device)
+    wp, wn = ws.get(workspace_bytes(OP_FFN_FORWARD, M, d, F, T, C))
+    pk = _Packed()
+    _check(lib().twell_packed_view(wp, wn, M, d, F, T, C, ctypes.byref(pk)), "twell_packed_view")
+    base = ws.buf.data_ptr()
+    nT = F // T
+
+    def view(addr, n, dtype, shape):
+        off = addr - base
+        return ws.buf[off:off + n * torch.tensor([], dtype=dtype).element_size()].view(dtype).view(shape)
+
+    return Packed(
+        view(pk.vals, M * nT * C, torch.float32, (M, nT, C)),
+        view(pk.idx, M * nT * C, torch.uint8, (M, nT, C)),
+        view(pk.counts, M * nT, torch.int16, (M, nT)),
+        view(pk.ovf_rows, M, torch.int32, (M,)),
+        view(pk.n_ovf, 1, torch.int32, (1,)),
+        T,
+        C,
+    )

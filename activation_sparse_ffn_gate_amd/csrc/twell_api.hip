@@ -1,0 +1,275 @@
+// extern "C" entry points of libtwell.so: argument checks, workspace layout
+// and launch order. Declared and documented in include/twell.h.
+#include <stdint.h>
+
+#include "../../include/twell.h"
+#include "twell_internal.hpp"
+
+using twell::align256;
+
+namespace {
+
+constexpr int64_t kMaxM = int64_t(1) << 30;
+constexpr int64_t kMaxF = int64_t(1) << 24;
+
+struct Layout {
+  size_t ctrl = 0, vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0;
+  size_t total = 0;
+};
+
+size_t ctrl_bytes(int64_t M) { return twell::kCtrlBytes + align256(size_t(M) * 4); }
+
+// Offsets inside the workspace of each operation (all 256-byte aligned).
+Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t m = size_t(M), f = size_t(F);
+  const size_t nT = (T > 0) ? f / size_t(T) : 0;
+  switch (op) {
+    case TWELL_OP_GATE_PACK:
+      L.ctrl = take(ctrl_bytes(M));
+      break;
+    case TWELL_OP_FFN_FORWARD:
+      L.ctrl = take(ctrl_bytes(M));
+      L.vals = take(m * nT * size_t(C) * 4);
+      L.idx = take(m * nT * size_t(C));
+      L.counts = take(m * nT * 2);
+      L.ovf_rows = take(m * 4);
+      L.n_ovf = take(4);
+      L.h_hi = take(m * f * 2);
+      L.h_lo = take(m * f * 2);
+      break;
+    case TWELL_OP_DENSE_FFN:
+      L.h_hi = take(m * f * 2);
+      break;
+    case TWELL_OP_DENSE_FALLBACK:
+      L.h_hi = take(m * f * 2);
+      L.h_lo = take(m * f * 2);
+      break;
+    default:
+      return L;
+  }
+  L.total = off;
+  return L;
+}
+
+int check_dims(int64_t M, int64_t d, int64_t F) {
+  if (M < 0 || d <= 0 || F <= 0) return TWELL_E_INVALID_ARG;
+  if (M > kMaxM || F > kMaxF) return TWELL_E_INVALID_ARG;
+  if (d % 256 != 0 || d > 8192 || !twell::fused_supports_d(int(d))) return TWELL_E_UNSUPPORTED;
+  return TWELL_OK;
+}
+
+int check_tc(int64_t F, int32_t T, int32_t C) {
+  if (T != 64 && T != 128) return TWELL_E_UNSUPPORTED;
+  if (F % T != 0) return TWELL_E_UNSUPPORTED;
+  if (C < 1 || C > T) return TWELL_E_UNSUPPORTED;
+  return TWELL_OK;
+}
+
+int check_ws(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C, void* ws, size_t ws_bytes) {
+  const Layout L = layout(op, M, F, T, C);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.total)
+    return TWELL_E_WORKSPACE;
+  return TWELL_OK;
+}
+
+bool packed_ok(const twell_packed* p) {
+  return p && p->vals && p->idx && p->counts && p->ovf_rows && p->n_ovf;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+twell_packed packed_in_ws(void* ws, const Layout& L) {
+  twell_packed p;
+  p.vals = at<float>(ws, L.vals);
+  p.idx = at<uint8_t>(ws, L.idx);
+  p.counts = at<uint16_t>(ws, L.counts);
+  p.ovf_rows = at<int32_t>(ws, L.ovf_rows);
+  p.n_ovf = at<int32_t>(ws, L.n_ovf);
+  return p;
+}
+
+int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F, int32_t T,
+                   int32_t C, const twell_packed* out, float* z_debug, uint32_t* ctrl,
+                   hipStream_t s) {
+  if (M == 0) return hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
+  twell::GateArgs a;
+  a.x = x;
+  a.Wg = Wg;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.vals = out->vals;
+  a.idx = out->idx;
+  a.counts = out->counts;
+  a.ovf_rows = out->ovf_rows;
+  a.n_ovf = out->n_ovf;
+  a.ctrl = ctrl;
+  a.z_debug = z_debug;
+  return hip_status(twell::launch_gate_pack(a, s));
+}
+
+int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
+               int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s) {
+  if (M == 0) return TWELL_OK;
+  twell::FusedArgs a;
+  a.x = x;
+  a.WuT = WuT;
+  a.Wd = Wd;
+  a.vals = in->vals;
+  a.idx = in->idx;
+  a.counts = in->counts;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.y = y;
+  return hip_status(twell::launch_fused_updown(a, s));
+}
+
+int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+               int64_t M, int64_t d, int64_t F, const int32_t* rows, const int32_t* n_rows,
+               uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s) {
+  if (M == 0) return TWELL_OK;
+  twell::DenseArgs a;
+  a.x = x;
+  a.Wg = Wg;
+  a.WuT = WuT;
+  a.Wd = Wd;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.rows = rows;
+  a.n_rows = n_rows;
+  a.h_hi = h_hi;
+  a.h_lo = h_lo;
+  a.y = y;
+  return hip_status(twell::launch_dense(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
+                    int32_t T, int32_t C, const twell_packed* out, float* z_debug, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !Wg || !packed_ok(out)) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_GATE_PACK, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  const Layout L = layout(TWELL_OP_GATE_PACK, M, F, T, C);
+  return gate_pack_impl(x, Wg, M, d, F, T, C, out, z_debug, at<uint32_t>(workspace, L.ctrl),
+                        static_cast<hipStream_t>(stream));
+}
+
+int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
+                       const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                       int32_t C, float* y, void* stream) {
+  if (!x || !WuT || !Wd || !y || !in || !in->vals || !in->idx || !in->counts) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st != TWELL_OK) return st;
+  return fused_impl(x, WuT, Wd, in, M, d, F, T, C, y, static_cast<hipStream_t>(stream));
+}
+
+int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                         const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
+                         int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !Wg || !WuT || !Wd || !y || !in || !in->ovf_rows || !in->n_ovf) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0);
+  return dense_impl(x, Wg, WuT, Wd, M, d, F, in->ovf_rows, in->n_ovf, at<uint16_t>(workspace, L.h_hi),
+                    at<uint16_t>(workspace, L.h_lo), y, static_cast<hipStream_t>(stream));
+}
+
+int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                      const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
+                      float* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !Wg || !WuT || !Wd || !y) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  if (M == 0) return TWELL_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
+  const twell_packed p = packed_in_ws(workspace, L);
+  st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, at<uint32_t>(workspace, L.ctrl), s);
+  if (st != TWELL_OK) return st;
+  st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
+  if (st != TWELL_OK) return st;
+  return dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
+                    at<uint16_t>(workspace, L.h_lo), y, s);
+}
+
+int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                            const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !Wg || !WuT || !Wd || !y) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FFN, M, F, 0, 0, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  const Layout L = layout(TWELL_OP_DENSE_FFN, M, F, 0, 0);
+  return dense_impl(x, Wg, WuT, Wd, M, d, F, nullptr, nullptr, at<uint16_t>(workspace, L.h_hi),
+                    nullptr, y, static_cast<hipStream_t>(stream));
+}
+
+size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
+  if (check_dims(M, d, F) != TWELL_OK) return 0;
+  if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD) {
+    if (check_tc(F, T, C) != TWELL_OK) return 0;
+  } else if (op == TWELL_OP_DENSE_FFN || op == TWELL_OP_DENSE_FALLBACK) {
+    if (F % 64 != 0) return 0;
+    T = 0;
+    C = 0;
+  } else {
+    return 0;
+  }
+  return layout(op, M, F, T, C).total;
+}
+
+int twell_packed_view(void* workspace, size_t ws_bytes, int64_t M, int64_t d, int64_t F,
+                      int32_t T, int32_t C, twell_packed* out) {
+  if (!out) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  *out = packed_in_ws(workspace, layout(TWELL_OP_FFN_FORWARD, M, F, T, C));
+  return TWELL_OK;
+}
+
+const char* twell_status_string(int32_t status) {
+  switch (status) {
+    case TWELL_OK: return "ok";
+    case TWELL_E_INVALID_ARG: return "invalid argument (null pointer or bad dimension)";
+    case TWELL_E_UNSUPPORTED: return "unsupported shape (T, C, F % T or d)";
+    case TWELL_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TWELL_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t twell_abi_version(void) { return TWELL_ABI_VERSION; }
+
+}  // extern "C"

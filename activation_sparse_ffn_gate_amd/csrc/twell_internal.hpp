@@ -1,0 +1,62 @@
+// Host-side launch helpers of libtwell (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace twell {
+
+// Control block of the gate kernel's overflow set, kept in the workspace:
+// ctrl[0] = entries appended this call, ctrl[1] = workgroups finished,
+// followed by one dedup flag per row. Zero between calls.
+constexpr size_t kCtrlBytes = 256;
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct GateArgs {
+  const uint16_t* x;
+  const uint16_t* Wg;
+  int M, d, F, T, C;
+  float* vals;
+  uint8_t* idx;
+  uint16_t* counts;
+  int32_t* ovf_rows;
+  int32_t* n_ovf;
+  uint32_t* ctrl;   // kCtrlBytes, then flags[M]
+  float* z_debug;   // nullable
+};
+
+struct FusedArgs {
+  const uint16_t* x;
+  const uint16_t* WuT;
+  const uint16_t* Wd;
+  const float* vals;
+  const uint8_t* idx;
+  const uint16_t* counts;
+  int M, d, F, T, C;
+  float* y;
+};
+
+// Dense gated FFN over a list of rows (all rows, or the overflow rows).
+struct DenseArgs {
+  const uint16_t* x;
+  const uint16_t* Wg;
+  const uint16_t* WuT;
+  const uint16_t* Wd;
+  int M, d, F;
+  const int32_t* rows;    // nullptr: rows 0..M-1
+  const int32_t* n_rows;  // device count of `rows` (when rows != nullptr)
+  uint16_t* h_hi;         // [M, F] bf16 hidden (or its high part)
+  uint16_t* h_lo;         // [M, F] low part; nullptr: plain bf16 hidden
+  float* y;
+};
+
+hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
+hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
+hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);
+
+bool fused_supports_d(int d);
+
+}  // namespace twell

@@ -1,0 +1,229 @@
+"""Throughput of the TwELL sparse gated-FFN forward on one MI355X.
+
+One step = one twell_ffn_forward (gate GEMM + TwELL packing, fused up+down
+over the packed non-zeros, dense fallback of overflow rows) over the whole
+synthetic layer, inputs resident in HBM. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is the 1.5B-like layer: M=4096 tokens, d=2048, F=8192,
+about 29 active gate units per token, T=128, C=16.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse FFN fwd tokens/s at d=2048,F=8192,~29 nnz/tok; % of HBM/MFMA roofline"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ffn1p5b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--only", choices=["forward", "gate", "fused", "dense", "copy"], default=None,
+                    help="run only this leg (for profiler runs); prints a short line")
+    ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
+    return ap.parse_args()
+
+
+def time_loop(fn, steps, stream):
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same layer's rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    w = inp.workload
+    chunk = 128
+    rows_done = 0
+    t0 = time.perf_counter()
+    while rows_done < w.M and time.perf_counter() - t0 < budget_s:
+        rows = np.arange(rows_done, min(rows_done + chunk, w.M))
+        Z = O.gate_preactivations(inp.x, inp.Wg, rows=rows)
+        p = O.pack_twell(Z.astype(np.float32), w.T, w.C)
+        O.dense_gated_ffn(inp.x, inp.Wg, inp.WuT, inp.Wd, rows=rows)
+        O.ffn_from_twell(p, inp.x[rows], inp.Wg, inp.WuT, inp.Wd)
+        rows_done += len(rows)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round(rows_done / dt, 2),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {rows_done} of {w.M} tokens of {w.name}: fp64 gate, TwELL pack, "
+                  f"fp64 dense FFN and sparse FFN from the packing ({dt:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards by tokens with no communication)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def td(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, Wg, WuT, Wd = (td(a) for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+    y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ws_fwd = tw.Workspace(dev)
+    ws_gate = tw.Workspace(dev)
+    ws_dense = tw.Workspace(dev)
+    packed = tw.Packed.empty(w.M, w.F, w.T, w.C, dev)
+
+    fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_fwd)  # noqa: E731
+    gate = lambda: tw.gate_pack(x, Wg, w.T, w.C, out=packed, workspace=ws_gate)  # noqa: E731
+    fused = lambda: tw.fused_updown(x, WuT, Wd, packed, y=y)  # noqa: E731
+    fallback = lambda: tw.dense_fallback(x, Wg, WuT, Wd, packed, y, workspace=ws_dense)  # noqa: E731
+    y_dense = torch.empty_like(y)
+    dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y_dense, workspace=ws_dense)  # noqa: E731
+
+    if args.only is not None:
+        if args.only == "copy":
+            n = args.copy_mb * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            fn = lambda: dst.copy_(src)  # noqa: E731
+        else:
+            fn = {"forward": fwd, "gate": gate, "fused": fused, "dense": dense}[args.only]
+            gate()  # the fused leg reads a packing
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = time_loop(fn, args.steps, stream)
+        print(json.dumps({"only": args.only, "ms_per_call": round(ms, 5), "steps": args.steps}))
+        return 0
+
+    # ---------------------------------------------------------------- headline
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    value = w.M * args.steps / elapsed
+
+    # ------------------------------------------------- per-kernel (HIP events)
+    gate()
+    torch.cuda.synchronize()
+    counts = packed.counts.cpu().numpy().view(np.uint16).astype(np.int64)
+    n_ovf = int(packed.n_ovf.item())
+    fit = counts.max(axis=1) <= w.C
+    nnz_fit = int(counts[fit].sum())
+    nnz_all = int(counts.sum())
+    k_steps = max(args.steps, 20)
+    for fn in (gate, fused, fallback, dense):
+        fn()
+    torch.cuda.synchronize()
+    t_gate = time_loop(gate, k_steps, stream)
+    t_fused = time_loop(fused, k_steps, stream)
+    t_fb = time_loop(fallback, k_steps, stream)
+    t_dense = time_loop(dense, k_steps, stream)
+
+    nT = w.F // w.T
+    gate_flops = 2.0 * w.M * w.d * w.F
+    # algorithmic bytes of one fused launch: each stored unit gathers one WuT and
+    # one Wd row (2 * 2d bytes); each row reads x (2d), its counts (2 nT) and
+    # stored slots (5 bytes each) and writes y (4d)
+    fused_bytes = nnz_fit * 4.0 * w.d + fit.sum() * (2.0 * w.d + 4.0 * w.d) + w.M * 2.0 * nT + nnz_fit * 5.0
+    gate_tflops = gate_flops / (t_gate * 1e-3) / 1e12
+    fused_gbs = fused_bytes / (t_fused * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        traffic = rec.get(args.workload, {}).get("fused" if t_fused >= t_gate else "gate")
+    if t_fused >= t_gate:
+        roof = {"kernel": "fused_updown", "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(gate_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C,
+                   "mean_nnz_target": round(w.mean_nnz, 3), "parallelism": "none"},
+        "roofline": roof,
+        "kernels": {
+            "gate_pack_ms": round(t_gate, 5),
+            "gate_pack_tflops": round(gate_tflops, 1),
+            "gate_pack_mfma_frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4),
+            "fused_updown_ms": round(t_fused, 5),
+            "fused_updown_gbs": round(fused_gbs, 1),
+            "fused_updown_hbm_frac": round(fused_gbs / PEAK_HBM_GBS, 4),
+            "dense_fallback_ms": round(t_fb, 5),
+            "nnz_per_token": round(nnz_all / w.M, 3),
+            "overflow_rows": n_ovf,
+        },
+        "dense_baseline": {
+            "ms": round(t_dense, 5),
+            "tokens_per_s": round(w.M / (t_dense * 1e-3), 1),
+            "tflops": round(3 * gate_flops / (t_dense * 1e-3) / 1e12, 1),
+            "speedup_sparse_vs_dense": round(t_dense / ms_step, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

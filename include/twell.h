@@ -1,0 +1,148 @@
+/* twell.h — C ABI of libtwell.so: TwELL sparse gated-FFN forward on MI355X (gfx950).
+ *
+ * The layer computed is the ReLU-gated FFN
+ *     y = (ReLU(x Wg^T) ⊙ (x Wu^T)) Wd
+ * (a Llama-style gated FFN with its SiLU gate replaced by ReLU: Tencent Cloud
+ * article "一文读懂 NVIDIA 与 Sakana AI 联手打造的稀疏 LLM 黑科技", section 1;
+ * aimodeling.com TwELL news summary, paragraph 4). When the gate is mostly
+ * zero, the gate GEMM packs its non-zeros per column tile into TwELL in its
+ * epilogue and a fused kernel does the up and down projections over the packed
+ * non-zeros only (Telegram post on TwELL at tgviewer.app, parts "Вот тут и
+ * решает TwELL" and "Инференс"; aimodeling.com summary, paragraph 3).
+ *
+ * Conventions for every entry point
+ *  - bf16 tensors are passed as raw uint16_t bit patterns.
+ *  - Every array argument is a DEVICE pointer to row-major, contiguous memory
+ *    allocated and owned by the caller. The library never allocates or frees
+ *    memory and keeps no state between calls.
+ *  - Weights are all [F, d] row-major, row j belonging to hidden unit j:
+ *      Wg  = gate_proj.weight, WuT = up_proj.weight,
+ *      Wd  = down_proj.weight transposed (row j = the d outputs unit j feeds).
+ *    So every per-unit gather of the fused kernel reads one contiguous row.
+ *  - x is [M, d] bf16; y is [M, d] fp32.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream). Errors found on the host are returned
+ *    before anything is enqueued; execution errors surface at the caller's
+ *    stream synchronisation. No exception crosses the ABI.
+ *  - Shape limits: M >= 0 and M < 2^31; d % 256 == 0 and 256 <= d <= 8192;
+ *    F > 0 with F % T == 0; T in {64, 128}; 1 <= C <= T.
+ *  - Workspace: a caller-owned device buffer of at least
+ *    twell_workspace_bytes(op, ...) bytes, 256-byte aligned. It MUST be
+ *    zero-filled before its first use; every call leaves its control block
+ *    zeroed again when it completes (in stream order). One workspace must not
+ *    be used by two calls that may run concurrently.
+ */
+#ifndef TWELL_H_
+#define TWELL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWELL_ABI_VERSION 1
+
+/* Status codes. */
+#define TWELL_OK 0
+#define TWELL_E_INVALID_ARG (-1) /* null pointer, negative or zero dimension, M too large */
+#define TWELL_E_UNSUPPORTED (-2) /* F % T != 0, T not in {64,128}, C out of [1,T], d not supported */
+#define TWELL_E_WORKSPACE (-3)   /* workspace null, misaligned or smaller than required */
+#define TWELL_E_HIP (-4)         /* a HIP launch failed (hipGetLastError) */
+
+/* Operations for twell_workspace_bytes. */
+#define TWELL_OP_GATE_PACK 0
+#define TWELL_OP_FFN_FORWARD 1
+#define TWELL_OP_DENSE_FFN 2
+#define TWELL_OP_DENSE_FALLBACK 3
+
+/* TwELL packing of ReLU(x Wg^T) with tile width T and capacity C
+ * (the format: tgviewer.app Telegram post, part "Вот тут и решает TwELL";
+ * Tencent Cloud article, section 2). nT = F / T tiles per row.
+ *   vals   [M, nT, C] fp32  gate value ReLU(z) of the s-th active unit of tile t
+ *   idx    [M, nT, C] u8    its tile-local column (0..T-1), strictly ascending in s
+ *   counts [M, nT]    u16   number of active units (z > 0) in the tile, NOT clamped
+ *   ovf_rows [M]      i32   rows with some counts[r][t] > C, order unspecified
+ *   n_ovf  [1]        i32   number of valid entries of ovf_rows
+ * Only slots s < min(counts, C) are written; other slots are left untouched.
+ * Overflow rows still hold the first C active units of every tile. */
+typedef struct twell_packed {
+  float* vals;
+  uint8_t* idx;
+  uint16_t* counts;
+  int32_t* ovf_rows;
+  int32_t* n_ovf;
+} twell_packed;
+
+/* Gate GEMM with the TwELL packing in its epilogue (aimodeling.com summary,
+ * paragraph 3; pulsen.vercel.app article, paragraph on tile matching; Tencent
+ * Cloud article, section 2): z = x Wg^T in fp32 from bf16 MFMA products, then
+ * ReLU and the per-tile packing of `out`, in one launch and without writing z.
+ * z_debug: optional [M, F] fp32; when non-NULL every pre-activation z is also
+ * stored (for bit-exact checks of the packing), otherwise pass NULL.
+ * workspace: >= twell_workspace_bytes(TWELL_OP_GATE_PACK, ...). */
+int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
+                    int32_t T, int32_t C, const twell_packed* out, float* z_debug,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Fused up+down projection over a TwELL packing (tgviewer.app Telegram post,
+ * part "Инференс"; aimodeling.com summary, paragraph 3): for every row that is
+ * not an overflow row, y[r] = sum over stored units j of
+ * g_j * (x[r] . WuT[j]) * Wd[j], with fp32 accumulation. The hidden vector is
+ * never written to memory. Rows with some count > C are NOT written (the dense
+ * fallback owns them). `in` is what twell_gate_pack produced with the same
+ * M, F, T, C. */
+int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
+                       const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                       int32_t C, float* y, void* stream);
+
+/* Dense fallback for the overflow rows of a packing (rows that do not fit the
+ * sparse block go to a dense path: tgviewer.app Telegram post, part
+ * "Обучение"; Tencent Cloud article, section 3). For the *in->n_ovf rows listed
+ * in in->ovf_rows it computes y[r] = (ReLU(x_r Wg^T) ⊙ x_r WuT^T) Wd with bf16
+ * MFMA products, fp32 accumulation and the hidden vector carried as a bf16
+ * hi/lo pair. n_ovf is read on the device (no host synchronisation); other rows
+ * of y are untouched.
+ * workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FALLBACK, ...). */
+int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                         const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
+                         int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* The whole sparse forward: twell_gate_pack, twell_fused_updown and
+ * twell_dense_fallback on one stream, with the packing kept in the workspace
+ * (see twell_packed_view). y [M, d] fp32 is fully written.
+ * workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
+int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                      const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
+                      float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Dense MFMA gated-FFN baseline (the comparator the pages measure against:
+ * dense matmuls, tgviewer.app Telegram post, paragraph after "Обучение"):
+ * h = ReLU(x Wg^T) ⊙ (x WuT^T) rounded to bf16 and written to the workspace,
+ * then y = h Wd in fp32. workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FFN, ...). */
+int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                            const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs (0 for invalid arguments). T and C are
+ * ignored for TWELL_OP_DENSE_FFN and TWELL_OP_DENSE_FALLBACK. */
+size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C);
+
+/* Where twell_ffn_forward keeps its packing inside `workspace` (host-side
+ * pointer arithmetic only; nothing is enqueued). Valid after that call has
+ * completed on its stream. */
+int twell_packed_view(void* workspace, size_t ws_bytes, int64_t M, int64_t d, int64_t F,
+                      int32_t T, int32_t C, twell_packed* out);
+
+/* Static string for a status code; never NULL. */
+const char* twell_status_string(int32_t status);
+
+/* TWELL_ABI_VERSION of the built library. */
+int32_t twell_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H_ */

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/twell.h declares, sizes workspaces, and rejects bad arguments before
+anything is enqueued (every call below fails validation on the host)."""
+
+import ctypes
+
+import pytest
+
+import activation_sparse_ffn_gate_amd as tw
+from activation_sparse_ffn_gate_amd._lib import _Packed
+
+OK, E_ARG, E_UNSUP, E_WS = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def test_exports_every_declared_function():
+    L = tw.lib()
+    names = tw.header_functions()
+    assert "twell_gate_pack" in names and "twell_dense_ffn_forward" in names
+    for n in names:
+        assert hasattr(L, n), f"libtwell.so does not export {n}"
+
+
+def test_abi_version_and_status_strings():
+    L = tw.lib()
+    assert L.twell_abi_version() == 1
+    for s in (OK, E_ARG, E_UNSUP, E_WS, -4):
+        assert tw.status_string(s)
+    assert tw.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("M,d,F,T,C", [(4096, 2048, 8192, 128, 16), (64, 256, 1024, 64, 8), (0, 256, 128, 64, 1)])
+def test_workspace_sizes(M, d, F, T, C):
+    nT = F // T
+    g = tw.workspace_bytes(tw.OP_GATE_PACK, M, d, F, T, C)
+    f = tw.workspace_bytes(tw.OP_FFN_FORWARD, M, d, F, T, C)
+    dn = tw.workspace_bytes(tw.OP_DENSE_FFN, M, d, F)
+    fb = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, M, d, F)
+    assert g >= 256 + 4 * M and g % 256 == 0
+    assert f >= g + M * nT * C * 5 + M * nT * 2 + 4 * M + 4 * M * F
+    assert dn >= 2 * M * F and fb >= 4 * M * F
+    assert f % 256 == 0 and dn % 256 == 0
+
+
+@pytest.mark.parametrize(
+    "args,want",
+    [
+        ((4096, 2048, 8192, 100, 16), 0),  # T not 64/128
+        ((4096, 2048, 8192, 128, 0), 0),  # C < 1
+        ((4096, 2048, 8192, 128, 129), 0),  # C > T
+        ((4096, 2048, 8000, 128, 16), 0),  # F % T
+        ((4096, 2000, 8192, 128, 16), 0),  # d % 256
+        ((-1, 2048, 8192, 128, 16), 0),  # M < 0
+    ],
+)
+def test_workspace_bytes_rejects(args, want):
+    assert tw.workspace_bytes(tw.OP_FFN_FORWARD, *args) == want
+
+
+def _packed():
+    return _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+
+
+def test_gate_pack_validation():
+    L = tw.lib()
+    pk = _packed()
+    ok_ws = tw.workspace_bytes(tw.OP_GATE_PACK, 256, 256, 1024, 64, 8)
+    call = lambda *a: L.twell_gate_pack(*a)  # noqa: E731
+    assert call(None, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_ARG
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, None, None, FAKE, ok_ws, None) == E_ARG
+    bad = _Packed(FAKE.value, 0, FAKE.value, FAKE.value, FAKE.value)
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(bad), None, FAKE, ok_ws, None) == E_ARG
+    assert call(FAKE, FAKE, -5, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_ARG
+    assert call(FAKE, FAKE, 256, 256, 1000, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 32, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 65, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 300, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, None, ok_ws, None) == E_WS
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws - 1, None) == E_WS
+    mis = ctypes.c_void_p(FAKE.value + 8)
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, mis, ok_ws, None) == E_WS
+
+
+def test_forward_validation():
+    L = tw.lib()
+    ws = tw.workspace_bytes(tw.OP_FFN_FORWARD, 256, 256, 1024, 64, 8)
+    f = L.twell_ffn_forward
+    assert f(FAKE, FAKE, None, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, ws, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, None, FAKE, ws, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 96, 8, FAKE, FAKE, ws, None) == E_UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, ws - 256, None) == E_WS
+    d = L.twell_dense_ffn_forward
+    dws = tw.workspace_bytes(tw.OP_DENSE_FFN, 256, 256, 1024)
+    assert d(FAKE, FAKE, FAKE, FAKE, 256, 256, 1000, FAKE, FAKE, dws, None) == E_UNSUP
+    assert d(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, FAKE, FAKE, dws - 1, None) == E_WS
+    u = L.twell_fused_updown
+    pk = _packed()
+    assert u(FAKE, FAKE, FAKE, None, 256, 256, 1024, 64, 8, FAKE, None) == E_ARG
+    assert u(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 0, FAKE, None) == E_UNSUP
+    fb = L.twell_dense_fallback
+    fws = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, 256, 256, 1024)
+    assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, FAKE, fws - 1, None) == E_WS
+    assert fb(FAKE, FAKE, FAKE, FAKE, None, 256, 256, 1024, FAKE, FAKE, fws, None) == E_ARG
+
+
+def test_packed_view_is_host_arithmetic():
+    L = tw.lib()
+    M, d, F, T, C = 256, 256, 1024, 64, 8
+    ws = tw.workspace_bytes(tw.OP_FFN_FORWARD, M, d, F, T, C)
+    base = 0x10000000
+    pk = _Packed()
+    assert L.twell_packed_view(ctypes.c_void_p(base), ws, M, d, F, T, C, ctypes.byref(pk)) == OK
+    ptrs = [pk.vals, pk.idx, pk.counts, pk.ovf_rows, pk.n_ovf]
+    assert all(p % 256 == 0 for p in ptrs)
+    assert all(base <= p < base + ws for p in ptrs)
+    nT = F // T
+    assert pk.idx - pk.vals >= M * nT * C * 4 and pk.counts - pk.idx >= M * nT * C
+    assert L.twell_packed_view(ctypes.c_void_p(base), ws - 1, M, d, F, T, C, ctypes.byref(pk)) == E_WS
