@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     Packed,
     TwellError,
     Workspace,
+    ctrl_bytes,
     dense_fallback,
     dense_ffn_forward,
     ffn_forward,

@@ -43,9 +43,10 @@ _SIGNATURES = {
     "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
     "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P]),
-    "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "twell_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32]),
+    "twell_ctrl_bytes": (_SZ, [_I64]),
     "twell_packed_view": (ctypes.c_int, [_P, _SZ, _I64, _I64, _I64, _I32, _I32, _PK]),
     "twell_status_string": (ctypes.c_char_p, [_I32]),
     "twell_abi_version": (ctypes.c_int32, []),
@@ -92,6 +93,10 @@ def workspace_bytes(op: int, M: int, d: int, F: int, T: int = 0, C: int = 0) -> 
     return int(lib().twell_workspace_bytes(op, M, d, F, T, C))
 
 
+def ctrl_bytes(M: int) -> int:
+    return int(lib().twell_ctrl_bytes(M))
+
+
 # --------------------------------------------------------------- torch-facing API
 def _torch():
     import torch
@@ -118,7 +123,7 @@ def _bf16(t, name, shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return _ptr(t)
+    return _dptr(t)
 
 
 def _f32_out(t, name, shape, device):
@@ -152,32 +157,34 @@ class Packed:
             torch.empty((M, nT, C), dtype=torch.float32, device=device),
             torch.empty((M, nT, C), dtype=torch.uint8, device=device),
             torch.empty((M, nT), dtype=torch.int16, device=device),
-            torch.empty((max(M, 1),), dtype=torch.int32, device=device),
+            torch.empty((M,), dtype=torch.int32, device=device),
             torch.empty((1,), dtype=torch.int32, device=device),
             T,
             C,
         )
 
     def _c(self) -> _Packed:
-        return _Packed(self.vals.data_ptr(), self.idx.data_ptr(), self.counts.data_ptr(),
-                       self.ovf_rows.data_ptr(), self.n_ovf.data_ptr())
+        return _Packed(*(_dptr(t).value or 0 for t in (self.vals, self.idx, self.counts, self.ovf_rows, self.n_ovf)))
 
 
 class Workspace:
-    """Zero-filled, 256-byte aligned device scratch, grown on demand and reused.
+    """256-byte aligned device scratch, grown on demand and reused.
 
-    The library leaves the control block zeroed after each call, so the buffer
-    is zero-filled only when it is (re)allocated.
+    zeroed=True makes a control block: zero-filled whenever it is (re)allocated;
+    the library leaves it zero-filled after every call, and it is used for
+    nothing else.
     """
 
-    def __init__(self, device=None):
+    def __init__(self, device=None, zeroed=False):
         self.device = device
+        self.zeroed = zeroed
         self.buf = None
 
     def get(self, nbytes: int):
         torch = _torch()
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 256) + 256, dtype=torch.uint8, device=self.device)
+        if self.buf is None or self.buf.numel() < nbytes + 256:
+            make = torch.zeros if self.zeroed else torch.empty
+            self.buf = make(max(nbytes, 256) + 256, dtype=torch.uint8, device=self.device)
         base = self.buf.data_ptr()
         off = (-base) % 256
         return ctypes.c_void_p(base + off), self.buf.numel() - off
@@ -186,17 +193,25 @@ class Workspace:
 _WS: dict = {}
 
 
-def _workspace(ws, device):
+def _workspace(ws, device, zeroed=False):
     if ws is None:
-        key = (device.type, device.index)
+        key = (device.type, device.index, zeroed)
         if key not in _WS:
-            _WS[key] = Workspace(device)
+            _WS[key] = Workspace(device, zeroed=zeroed)
         ws = _WS[key]
+    elif ws.zeroed != zeroed:
+        raise ValueError("a control block must be a Workspace(zeroed=True) used for nothing else")
     return ws
 
 
-def gate_pack(x, Wg, T: int, C: int, out: Packed | None = None, z_debug=None, workspace=None) -> Packed:
-    """twell_gate_pack. z_debug: None, or a float32 [M, F] tensor to receive z."""
+def _dptr(t):
+    """Device pointer of a tensor, NULL for an empty one."""
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+def gate_pack(x, Wg, T: int, C: int, out: Packed | None = None, z_debug=None, ctrl=None) -> Packed:
+    """twell_gate_pack. z_debug: None, or a float32 [M, F] tensor to receive z.
+    ctrl: a Workspace(zeroed=True) control block (a per-device one by default)."""
     M, d = x.shape
     F = Wg.shape[0]
     px, pw = _bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d))
@@ -204,11 +219,11 @@ def gate_pack(x, Wg, T: int, C: int, out: Packed | None = None, z_debug=None, wo
     pz = ctypes.c_void_p(0)
     if z_debug is not None:
         _f32_out(z_debug, "z_debug", (M, F), x.device)
-        pz = _ptr(z_debug)
-    ws = _workspace(workspace, x.device)
-    wp, wn = ws.get(workspace_bytes(OP_GATE_PACK, M, d, F, T, C))
+        pz = _dptr(z_debug)
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
     pk = out._c()
-    _check(lib().twell_gate_pack(px, pw, M, d, F, T, C, ctypes.byref(pk), pz, wp, wn, _stream(x)), "twell_gate_pack")
+    _check(lib().twell_gate_pack(px, pw, M, d, F, T, C, ctypes.byref(pk), pz, cp, cn, _stream(x)), "twell_gate_pack")
     return out
 
 
@@ -218,7 +233,7 @@ def fused_updown(x, WuT, Wd, packed: Packed, y=None):
     args = (_bf16(x, "x", (M, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
     y = _f32_out(y, "y", (M, d), x.device)
     pk = packed._c()
-    _check(lib().twell_fused_updown(*args, ctypes.byref(pk), M, d, F, packed.T, packed.C, _ptr(y), _stream(x)),
+    _check(lib().twell_fused_updown(*args, ctypes.byref(pk), M, d, F, packed.T, packed.C, _dptr(y), _stream(x)),
            "twell_fused_updown")
     return y
 
@@ -231,19 +246,21 @@ def dense_fallback(x, Wg, WuT, Wd, packed: Packed, y, workspace=None):
     ws = _workspace(workspace, x.device)
     wp, wn = ws.get(workspace_bytes(OP_DENSE_FALLBACK, M, d, F))
     pk = packed._c()
-    _check(lib().twell_dense_fallback(*args, ctypes.byref(pk), M, d, F, _ptr(y), wp, wn, _stream(x)),
+    _check(lib().twell_dense_fallback(*args, ctypes.byref(pk), M, d, F, _dptr(y), wp, wn, _stream(x)),
            "twell_dense_fallback")
     return y
 
 
-def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None):
+def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None, ctrl=None):
     M, d = x.shape
     F = Wg.shape[0]
     args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
     y = _f32_out(y, "y", (M, d), x.device)
     ws = _workspace(workspace, x.device)
     wp, wn = ws.get(workspace_bytes(OP_FFN_FORWARD, M, d, F, T, C))
-    _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _ptr(y), wp, wn, _stream(x)), "twell_ffn_forward")
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, _stream(x)), "twell_ffn_forward")
     return y
 
 
@@ -254,7 +271,7 @@ def dense_ffn_forward(x, Wg, WuT, Wd, y=None, workspace=None):
     y = _f32_out(y, "y", (M, d), x.device)
     ws = _workspace(workspace, x.device)
     wp, wn = ws.get(workspace_bytes(OP_DENSE_FFN, M, d, F))
-    _check(lib().twell_dense_ffn_forward(*args, M, d, F, _ptr(y), wp, wn, _stream(x)), "twell_dense_ffn_forward")
+    _check(lib().twell_dense_ffn_forward(*args, M, d, F, _dptr(y), wp, wn, _stream(x)), "twell_dense_ffn_forward")
     return y
 
 

@@ -6,42 +6,51 @@
 // computes a tile of z = x Wg^T can pack its non-zeros right away: no second
 // launch, no synchronisation between workgroups, no dense z in memory.
 //
-// MI355X mapping. One workgroup (4 waves) computes a 256-token x 128-unit tile
-// with v_mfma_f32_32x32x16_bf16 over LDS-staged, double-buffered 32-wide K
-// chunks. Each wave owns 64 tokens x all 128 units of the tile, so every
-// (token, TwELL tile) row segment of 64 or 128 units lives inside one wave.
-// Packing then needs no LDS round trip: in the accumulator layout one register
-// holds, across the 64 lanes, 32 consecutive units of two tokens, so a 64-bit
-// ballot of (z > 0) gives both tokens' activity masks; popcounts of the masks
-// give the per-tile count and each lane's slot is the popcount of the mask bits
-// below it (ascending unit order). Values (fp32) and tile-local indices are
-// stored only for slots < C; the per-(token, tile) count is stored unclamped.
+// MI355X mapping. One workgroup (4 waves, one per SIMD) computes a 256-token x
+// 256-unit tile with v_mfma_f32_32x32x16_bf16; each wave owns a 128 x 128
+// quarter (16 accumulator blocks, kept in the AGPRs). K advances in 32-wide
+// chunks through a 4-stage LDS ring filled by gfx950's global_load_lds (16
+// bytes per lane straight into LDS, no register staging), issued three chunks
+// ahead so HBM/MALL latency hides behind the MFMAs. Each wave's 128 units are
+// whole TwELL tiles (T = 128 or 64), so every (token, tile) segment lives in
+// one wave and the packing needs no LDS round trip: in the accumulator layout
+// one register holds, across the 64 lanes, 32 consecutive units of two tokens,
+// so a 64-bit ballot of (z > 0) gives both tokens' activity masks; popcounts of
+// the masks give the per-tile count and each lane's slot is the popcount of
+// the mask bits below it (ascending unit order). Values (fp32) and tile-local
+// indices are stored only for slots < C; the per-(token, tile) count is stored
+// unclamped.
 //
 // Overflow rows (some tile count > C) are appended to a deduplicated list with
 // device-scope atomics. The last workgroup to finish publishes the list length
-// and clears the dedup flags, so the workspace control block is zero again
-// when the kernel ends and no separate clearing launch is needed.
+// and clears the dedup flags, so the control block is zero again when the
+// kernel ends and no separate clearing launch is needed.
 #include "twell_device.hpp"
 #include "twell_internal.hpp"
 
 namespace twell {
 namespace {
 
-constexpr int kBM = 256;  // tokens per workgroup tile
-constexpr int kBN = 128;  // hidden units per workgroup tile
-constexpr int kBK = 32;   // K chunk per LDS stage
-constexpr int kATileBytes = kBM * kBK * 2;
-constexpr int kBTileBytes = kBN * kBK * 2;
-constexpr int kStageBytes = kATileBytes + kBTileBytes;
+constexpr int kBM = 256;     // tokens per workgroup tile
+constexpr int kBN = 256;     // hidden units per workgroup tile
+constexpr int kBK = 32;      // K chunk per LDS stage
+constexpr int kStages = 5;   // LDS ring depth (5 x 32 KB = all 160 KB of LDS)
+constexpr int kAhead = kStages - 1;  // chunks in flight ahead of the one computed
+constexpr int kTileBytes = 256 * kBK * 2;  // one operand tile of a stage (16 KB)
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kDmaPerStage = 8;  // global_load_lds per thread per stage (4 for A, 4 for B)
 
 template <int kT, bool kDebug>
-__global__ __launch_bounds__(256, 2) void gate_pack_kernel(GateArgs a, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
-  __shared__ int s_last;
+__global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m) {
+  // One LDS object only: with a second one the compiler attaches alias scopes
+  // to LDS accesses and then makes every LDS read wait for all outstanding
+  // DMA, which would drain the pipeline below.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = w >> 1, wn = w & 1;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
   // contiguous run of tiles (token tiles fastest) so tiles that share a block
@@ -51,163 +60,227 @@ __global__ __launch_bounds__(256, 2) void gate_pack_kernel(GateArgs a, int tiles
   const int m0 = (lin % tiles_m) * kBM;
   const int n0 = (lin / tiles_m) * kBN;
 
-  // Global -> LDS staging: thread loads 16-byte piece (tid & 3) of rows
-  // (tid >> 2) + 64 i of the A (x) and B (Wg) chunks.
-  const int lrow = tid >> 2, lpc = tid & 3;
-  const uint16_t* pa[4];
-  bool va[4];
-  uint32_t sa[4];
+  // DMA addressing. A stage tile is 256 rows x 64 bytes; wave w fills the
+  // 16-row blocks 4w .. 4w+3 of each operand. In a block, lane l lands on row
+  // l / 4 at physical piece l % 4, which holds logical piece
+  // (l % 4) ^ lds_swz(row) of the swizzled layout (see lds_off). Rows past M
+  // or F read a valid row instead: their results are discarded. Addresses are
+  // a wave-uniform base plus a 32-bit per-lane byte offset (x and Wg are
+  // below 2 GiB, checked by the host).
+  uint32_t oa[4], ob[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = m0 + lrow + 64 * i;
-    va[i] = r < a.M;
-    pa[i] = a.x + static_cast<size_t>(va[i] ? r : 0) * a.d + lpc * 8;
-    sa[i] = lds_off(lrow + 64 * i, lpc);
+    const int row = (w * 4 + i) * 16 + (lane >> 2);
+    const uint32_t lp = static_cast<uint32_t>((lane & 3) ^ lds_swz(row)) * 16u;
+    oa[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * static_cast<uint32_t>(a.d * 2) + lp;
+    ob[i] = static_cast<uint32_t>(min(n0 + row, a.F - 1)) * static_cast<uint32_t>(a.d * 2) + lp;
   }
-  const uint16_t* pb[2];
-  bool vb[2];
-  uint32_t sb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = n0 + lrow + 64 * i;
-    vb[i] = r < a.F;
-    pb[i] = a.Wg + static_cast<size_t>(vb[i] ? r : 0) * a.d + lpc * 8;
-    sb[i] = lds_off(lrow + 64 * i, lpc);
-  }
-
-  u32x4_t ra[4], rb[2];
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = va[i] ? gload16(pa[i] + k0) : zero4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = vb[i] ? gload16(pb[i] + k0) : zero4;
+  const char* xbase = reinterpret_cast<const char*>(a.x);
+  const char* wbase = reinterpret_cast<const char*>(a.Wg);
+  // DMA j (0..7) of the batch filling buffer `buf` with chunk k0: j < 4 are
+  // the wave's A blocks, j >= 4 its B blocks.
+  auto dma = [&](int j, int buf, int k0) {
+    uint8_t* st = smem + buf * kStageBytes + w * 4 * 1024;
+    if (j < 4) dma16(reinterpret_cast<const uint16_t*>(xbase + k0 * 2 + oa[j]), st + j * 1024);
+    else dma16(reinterpret_cast<const uint16_t*>(wbase + k0 * 2 + ob[j - 4]), st + kTileBytes + (j - 4) * 1024);
   };
-  auto sstore = [&](int stage) {
-    uint8_t* As = smem + stage * kStageBytes;
-    uint8_t* Bs = As + kATileBytes;
+  auto issue = [&](int buf, int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_store16(As, sa[i], ra[i]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lds_store16(Bs, sb[i], rb[i]);
+    for (int j = 0; j < kDmaPerStage; ++j) dma(j, buf, k0);
   };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[4][4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
 
-  const int nk = a.d / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const uint8_t* As = smem + st * kStageBytes;
-    const uint8_t* Bs = As + kATileBytes;
+  // MFMA operands of one 16-wide k step: 4 A and 4 B fragments.
+  struct Frags {
+    u32x4_t a[4], b[4];
+  };
+  auto load_frags = [&](Frags& f, int buf, int ks) {
+    const uint8_t* As = smem + buf * kStageBytes;
+    const uint8_t* Bs = As + kTileBytes;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t af[2], bf[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) af[mb] = lds_frag(As, w * 64 + mb * 32, ks, lane);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bf[nb] = lds_frag(Bs, nb * 32, ks, lane);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(af[mb], bf[nb], acc[mb][nb]);
+    for (int i = 0; i < 4; ++i) {
+      f.a[i] = lds_frag(As, wm * 128 + i * 32, ks, lane);
+      f.b[i] = lds_frag(Bs, wn * 128 + i * 32, ks, lane);
     }
-    if (kt + 1 < nk) sstore(st ^ 1);
-    __syncthreads();
+  };
+  // One k step: the 16 MFMAs of `cur`; after each of the first 8 one fragment
+  // read of the next step (into `nxt`, buffer nbuf, half nks), after each of
+  // the last 8 one DMA of the batch for chunk dk0 (when kDma). The order is
+  // pinned so the matrix pipe is never idle behind an issue block.
+  auto step = [&](auto kDma, const Frags& cur, Frags& nxt, int nbuf, int nks, int dbuf, int dk0) {
+    const uint8_t* As = smem + nbuf * kStageBytes;
+    const uint8_t* Bs = As + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mb = i >> 2, nb = i & 3;
+      acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
+      if (i < 8) {
+        if (i & 1) nxt.b[i >> 1] = lds_frag(Bs, wn * 128 + (i >> 1) * 32, nks, lane);
+        else nxt.a[i >> 1] = lds_frag(As, wm * 128 + (i >> 1) * 32, nks, lane);
+      } else if constexpr (decltype(kDma)::value) {
+        dma(i - 8, dbuf, dk0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(f.a[mb], f.b[nb], acc[mb][nb]);
+  };
+  constexpr std::true_type with_dma{};
+  constexpr std::false_type no_dma{};
+
+  // Pipeline (nk >= 8 since d >= 256). Chunk kt's two k steps run from
+  // registers f0 / f1 while the next step's fragments load. Halfway through
+  // chunk kt every thread waits until its DMA of chunk kt + 1 has landed
+  // (later chunks may stay in flight); the barrier then publishes chunk
+  // kt + 1 and guarantees all waves are done with chunk kt - 1, whose buffer
+  // the DMA of chunk kt + kAhead reuses. Fragment reads never need waiting on
+  // at the barrier: the MFMAs that consumed them already waited.
+  const int nk = a.d / kBK;
+  // vmcnt allowing `chunks` later chunks (kDmaPerStage each) to stay in flight
+  auto wait_chunks = [](int chunks) {
+    if (chunks >= 3) waitcnt<3 * kDmaPerStage, 15>();
+    else if (chunks == 2) waitcnt<2 * kDmaPerStage, 15>();
+    else if (chunks == 1) waitcnt<kDmaPerStage, 15>();
+    else waitcnt<0, 15>();
+  };
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) issue(s, s * kBK);
+  wait_chunks(kAhead - 1);
+  raw_barrier();
+  Frags f0, f1;
+  load_frags(f0, 0, 0);
+  int kt = 0;
+  for (; kt < nk - kAhead; ++kt) {  // steady state: a DMA batch every chunk
+    step(no_dma, f0, f1, kt % kStages, 1, 0, 0);
+    waitcnt<(kAhead - 2) * kDmaPerStage, 15>();
+    raw_barrier();
+    step(with_dma, f1, f0, (kt + 1) % kStages, 0, (kt + kAhead) % kStages, (kt + kAhead) * kBK);
   }
+  for (; kt < nk - 1; ++kt) {  // drain: the last kAhead - 1 chunk boundaries
+    step(no_dma, f0, f1, kt % kStages, 1, 0, 0);
+    wait_chunks(nk - 2 - kt);
+    raw_barrier();
+    step(no_dma, f1, f0, (kt + 1) % kStages, 0, 0, 0);
+  }
+  step(no_dma, f0, f1, (nk - 1) % kStages, 1, 0, 0);
+  mma(f1);
 
   // ------------------------------------------------------------- epilogue
   const int half = lane >> 5;
   const int col = lane & 31;
-  const uint32_t below = (1u << col) - 1u;
   const int nT = a.F / kT;
-  constexpr int kTilesPerBlock = kBN / kT;     // 1 (T=128) or 2 (T=64)
-  constexpr int kBlocksPerTile = 4 / kTilesPerBlock;  // 32-unit blocks per TwELL tile
-  const int tile0 = n0 / kT;
-  const int wrow0 = m0 + w * 64;
+  constexpr int kTilesPerWave = 128 / kT;            // 1 (T=128) or 2 (T=64)
+  constexpr int kBlocksPerTile = 4 / kTilesPerWave;  // 32-unit blocks per TwELL tile
+  const int wcol0 = n0 + wn * 128;
+  const int tile0 = wcol0 / kT;
+  const int wrow0 = m0 + wm * 128;
   const int C = a.C;
+  const uint32_t row_slots = static_cast<uint32_t>(nT * C);  // slots per token
 
   if constexpr (kDebug) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = wrow0 + mb * 32 + acc_row(v, half);
-          const int cg = n0 + nb * 32 + col;
+          const int cg = wcol0 + nb * 32 + col;
           if (row < a.M && cg < a.F) a.z_debug[static_cast<size_t>(row) * a.F + cg] = acc[mb][nb][v];
         }
   }
 
-  // cnt[tt] of lane L = count of token wrow0 + L in TwELL tile tile0 + tt
-  uint32_t cnt[kTilesPerBlock];
+  // Tokens past M (only in the last row of tiles) must not count or pack.
+  if (wrow0 + 128 > a.M) {
 #pragma unroll
-  for (int tt = 0; tt < kTilesPerBlock; ++tt) cnt[tt] = 0;
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool ok = wrow0 + mb * 32 + acc_row(v, half) < a.M;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb][v] = ok ? acc[mb][nb][v] : 0.f;
+      }
+  }
 
+  // cnt[tt][h] of lane L = count of token wrow0 + 64 h + L in TwELL tile tile0 + tt
+  int cnt[kTilesPerWave][2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int tt = 0; tt < kTilesPerWave; ++tt) cnt[tt][0] = cnt[tt][1] = 0;
+
+  static_for<0, 64>([&](auto g) {
+    constexpr int mb = decltype(g)::value / 16, v = decltype(g)::value % 16;
+    uint64_t bal[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      uint64_t bal[4];
+    for (int nb = 0; nb < 4; ++nb) bal[nb] = __ballot(acc[mb][nb][v] > 0.f);
+    if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;  // both tokens inactive here
+    constexpr int rl_lo = mb * 32 + acc_row(v, 0);  // token of lanes 0-31; lanes 32-63: +4
+    constexpr int h = rl_lo >> 6, l_lo = rl_lo & 63;
+    const uint32_t row = static_cast<uint32_t>(wrow0 + rl_lo + 4 * half);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) bal[nb] = __ballot(acc[mb][nb][v] > 0.f);
-      if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) continue;  // both tokens inactive here
-      const int rl_lo = mb * 32 + acc_row(v, 0);  // token of lanes 0-31; lanes 32-63: +4
-      const int row = wrow0 + rl_lo + 4 * half;
-      uint32_t mk[4];
+    for (int tt = 0; tt < kTilesPerWave; ++tt) {
+      const int tile = tile0 + tt;
+      if (tile >= nT) continue;  // T = 64 and this half of the wave lies past F
+      uint32_t p_lo[kBlocksPerTile + 1], p_hi[kBlocksPerTile + 1];  // running prefixes
+      p_lo[0] = p_hi[0] = 0;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) mk[nb] = half ? static_cast<uint32_t>(bal[nb] >> 32) : static_cast<uint32_t>(bal[nb]);
+      for (int q = 0; q < kBlocksPerTile; ++q) {
+        const uint64_t bq = bal[tt * kBlocksPerTile + q];
+        p_lo[q + 1] = p_lo[q] + __popc(static_cast<uint32_t>(bq));
+        p_hi[q + 1] = p_hi[q] + __popc(static_cast<uint32_t>(bq >> 32));
+      }
+      cnt[tt][h] = writelane<l_lo>(cnt[tt][h], static_cast<int>(p_lo[kBlocksPerTile]));
+      cnt[tt][h] = writelane<l_lo + 4>(cnt[tt][h], static_cast<int>(p_hi[kBlocksPerTile]));
+      // Whether every active unit of both tokens fits in the C slots.
+      const bool fits = p_lo[kBlocksPerTile] <= static_cast<uint32_t>(C) &&
+                        p_hi[kBlocksPerTile] <= static_cast<uint32_t>(C);
+      const uint32_t base = row * row_slots + static_cast<uint32_t>(tile * C);
 #pragma unroll
-      for (int tt = 0; tt < kTilesPerBlock; ++tt) {
-        uint32_t c_lo = 0, c_hi = 0;
-#pragma unroll
-        for (int q = 0; q < kBlocksPerTile; ++q) {
-          c_lo += __popc(static_cast<uint32_t>(bal[tt * kBlocksPerTile + q]));
-          c_hi += __popc(static_cast<uint32_t>(bal[tt * kBlocksPerTile + q] >> 32));
-        }
-        if (lane == rl_lo) cnt[tt] = c_lo;
-        if (lane == rl_lo + 4) cnt[tt] = c_hi;
-        const int tile = tile0 + tt;
-        uint32_t pre = 0;
-#pragma unroll
-        for (int q = 0; q < kBlocksPerTile; ++q) {
-          const int nb = tt * kBlocksPerTile + q;
-          const uint32_t slot = pre + __popc(mk[nb] & below);
-          if (((mk[nb] >> col) & 1u) && slot < static_cast<uint32_t>(C) && row < a.M && tile < nT) {
-            const size_t o = (static_cast<size_t>(row) * nT + tile) * C + slot;
-            a.vals[o] = acc[mb][nb][v];
-            a.idx[o] = static_cast<uint8_t>(q * 32 + col);
-          }
-          pre += __popc(mk[nb]);
+      for (int q = 0; q < kBlocksPerTile; ++q) {
+        const int nb = tt * kBlocksPerTile + q;
+        const uint64_t bq = bal[nb];
+        if (bq == 0) continue;  // no active unit in these 32 columns
+        // slot = active units left of this one in the token's tile:
+        // earlier blocks (p_lo / p_hi) plus lower lanes of this block.
+        const uint32_t pre_hi = p_hi[q] - __popc(static_cast<uint32_t>(bq));
+        const uint32_t slot = mask_rank(bq) + (half ? pre_hi : p_lo[q]);
+        const float z = acc[mb][nb][v];
+        if (z > 0.f && (fits || slot < static_cast<uint32_t>(C))) {
+          store_at(a.vals, (base + slot) * 4u, z);
+          store_at(a.idx, base + slot, static_cast<uint8_t>(q * 32 + col));
         }
       }
     }
-  }
+  });
 
-  // Counts: lane L writes token wrow0 + L; overflow rows join the set.
+  // Counts: lane L writes tokens wrow0 + L and wrow0 + 64 + L; overflow rows
+  // join the set.
   uint32_t* flags = a.ctrl + kCtrlBytes / 4;
-  {
-    const int row = wrow0 + lane;
+  int appended = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = wrow0 + 64 * h + lane;
     if (row < a.M) {
       bool over = false;
 #pragma unroll
-      for (int tt = 0; tt < kTilesPerBlock; ++tt) {
+      for (int tt = 0; tt < kTilesPerWave; ++tt) {
         if (tile0 + tt < nT) {
-          a.counts[static_cast<size_t>(row) * nT + tile0 + tt] = static_cast<uint16_t>(cnt[tt]);
-          over |= cnt[tt] > static_cast<uint32_t>(C);
+          a.counts[static_cast<size_t>(row) * nT + tile0 + tt] = static_cast<uint16_t>(cnt[tt][h]);
+          over |= cnt[tt][h] > C;
         }
       }
       if (over && atomicExch(&flags[row], 1u) == 0u) {
+        appended = 1;
         const uint32_t pos = atomicAdd(&a.ctrl[0], 1u);
         // pos < M whenever the control block started zeroed, as the API requires
         if (pos < static_cast<uint32_t>(a.M))
@@ -216,15 +289,21 @@ __global__ __launch_bounds__(256, 2) void gate_pack_kernel(GateArgs a, int tiles
     }
   }
 
-  // The last workgroup publishes n_ovf and clears the control block.
+  // The last workgroup publishes n_ovf and clears the control block. Only a
+  // workgroup that appended rows has list entries to release to it. The
+  // stage buffers are idle now and hold the workgroup's flags.
+  int* sflag = reinterpret_cast<int*>(smem);  // [0] = last, [1 + w] = wave appended
+  const int wave_appended = __ballot(appended) != 0 ? 1 : 0;
+  __syncthreads();
+  if (lane == 0) sflag[1 + w] = wave_appended;
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
+    if (sflag[1] | sflag[2] | sflag[3] | sflag[4]) __threadfence();
     const uint32_t done = atomicAdd(&a.ctrl[1], 1u);
-    s_last = (done == static_cast<uint32_t>(gridDim.x) - 1u);
+    sflag[0] = (done == static_cast<uint32_t>(gridDim.x) - 1u);
   }
   __syncthreads();
-  if (s_last) {
+  if (sflag[0]) {
     __threadfence();
     uint32_t n = __hip_atomic_load(&a.ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     n = min(n, static_cast<uint32_t>(a.M));

@@ -13,7 +13,7 @@ constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxF = int64_t(1) << 24;
 
 struct Layout {
-  size_t ctrl = 0, vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0;
+  size_t vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0;
   size_t total = 0;
 };
 
@@ -32,10 +32,8 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
   const size_t nT = (T > 0) ? f / size_t(T) : 0;
   switch (op) {
     case TWELL_OP_GATE_PACK:
-      L.ctrl = take(ctrl_bytes(M));
       break;
     case TWELL_OP_FFN_FORWARD:
-      L.ctrl = take(ctrl_bytes(M));
       L.vals = take(m * nT * size_t(C) * 4);
       L.idx = take(m * nT * size_t(C));
       L.counts = take(m * nT * 2);
@@ -74,13 +72,21 @@ int check_tc(int64_t F, int32_t T, int32_t C) {
 
 int check_ws(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C, void* ws, size_t ws_bytes) {
   const Layout L = layout(op, M, F, T, C);
+  if (L.total == 0) return TWELL_OK;
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.total)
     return TWELL_E_WORKSPACE;
   return TWELL_OK;
 }
 
-bool packed_ok(const twell_packed* p) {
-  return p && p->vals && p->idx && p->counts && p->ovf_rows && p->n_ovf;
+int check_ctrl(int64_t M, void* ctrl, size_t n) {
+  if (ctrl == nullptr || (reinterpret_cast<uintptr_t>(ctrl) & 255u) != 0 || n < ctrl_bytes(M))
+    return TWELL_E_WORKSPACE;
+  return TWELL_OK;
+}
+
+// With M == 0 the row arrays are empty and may be NULL; n_ovf is still written.
+bool packed_ok(const twell_packed* p, int64_t M) {
+  return p && p->n_ovf && (M == 0 || (p->vals && p->idx && p->counts && p->ovf_rows));
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_E_HIP; }
@@ -166,22 +172,22 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
 extern "C" {
 
 int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
-                    int32_t T, int32_t C, const twell_packed* out, float* z_debug, void* workspace,
-                    size_t ws_bytes, void* stream) {
-  if (!x || !Wg || !packed_ok(out)) return TWELL_E_INVALID_ARG;
+                    int32_t T, int32_t C, const twell_packed* out, float* z_debug, void* ctrl,
+                    size_t ctrl_bytes_, void* stream) {
+  if ((M != 0 && !x) || !Wg || !packed_ok(out, M)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_GATE_PACK, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st != TWELL_OK) return st;
-  const Layout L = layout(TWELL_OP_GATE_PACK, M, F, T, C);
-  return gate_pack_impl(x, Wg, M, d, F, T, C, out, z_debug, at<uint32_t>(workspace, L.ctrl),
+  return gate_pack_impl(x, Wg, M, d, F, T, C, out, z_debug, static_cast<uint32_t*>(ctrl),
                         static_cast<hipStream_t>(stream));
 }
 
 int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
                        const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
                        int32_t C, float* y, void* stream) {
-  if (!x || !WuT || !Wd || !y || !in || !in->vals || !in->idx || !in->counts) return TWELL_E_INVALID_ARG;
+  if (!WuT || !Wd || !in) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!x || !y || !in->vals || !in->idx || !in->counts)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
   if (st != TWELL_OK) return st;
@@ -191,7 +197,8 @@ int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* W
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                          const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
                          int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream) {
-  if (!x || !Wg || !WuT || !Wd || !y || !in || !in->ovf_rows || !in->n_ovf) return TWELL_E_INVALID_ARG;
+  if (!Wg || !WuT || !Wd || !in || !in->n_ovf) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!x || !y || !in->ovf_rows)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
   if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0, workspace, ws_bytes);
@@ -203,17 +210,19 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
 
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                       const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
-                      float* y, void* workspace, size_t ws_bytes, void* stream) {
-  if (!x || !Wg || !WuT || !Wd || !y) return TWELL_E_INVALID_ARG;
+                      float* y, void* ctrl, size_t ctrl_bytes_, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   if (M == 0) return TWELL_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
-  st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, at<uint32_t>(workspace, L.ctrl), s);
+  st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
   st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
   if (st != TWELL_OK) return st;
@@ -224,7 +233,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
                             void* workspace, size_t ws_bytes, void* stream) {
-  if (!x || !Wg || !WuT || !Wd || !y) return TWELL_E_INVALID_ARG;
+  if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
   if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FFN, M, F, 0, 0, workspace, ws_bytes);
@@ -246,6 +255,11 @@ size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_
     return 0;
   }
   return layout(op, M, F, T, C).total;
+}
+
+size_t twell_ctrl_bytes(int64_t M) {
+  if (M < 0 || M > kMaxM) return 0;
+  return ctrl_bytes(M);
 }
 
 int twell_packed_view(void* workspace, size_t ws_bytes, int64_t M, int64_t d, int64_t F,

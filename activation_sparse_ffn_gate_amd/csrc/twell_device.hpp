@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace twell {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -48,6 +50,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ------------------------------------------------------------------ lane helpers
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Write the wave-uniform value `val` into lane LANE of `dst` (v_writelane_b32).
+template <int LANE>
+__device__ __forceinline__ int writelane(int dst, int val) {
+  static_assert(LANE >= 0 && LANE < 64, "lane");
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "i"(LANE));
+  return dst;
+}
+
+// Number of set bits of the 64-bit wave mask `m` in lanes below this lane.
+__device__ __forceinline__ uint32_t mask_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Stores through a wave-uniform base pointer and a 32-bit byte offset, so the
+// address needs no 64-bit vector arithmetic.
+template <class T>
+__device__ __forceinline__ void store_at(T* base, uint32_t byte_off, T v) {
+  *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = v;
 }
 
 // ------------------------------------------------------------------ wave collectives
@@ -88,11 +121,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ------------------------------------------------------------------ LDS tiles
-// A K-chunk of 32 bf16 per row is 64 bytes = four 16-byte pieces. Piece c of
-// row r is stored at piece (c ^ ((r >> 1) & 3)) so that the 32 rows read by an
-// MFMA fragment load spread over all banks.
+// A K-chunk of 32 bf16 per row is 64 bytes = four 16-byte pieces. An MFMA
+// fragment load reads one piece of 32 consecutive rows (ds_read_b128); the LDS
+// serves such a read 16 lanes (rows) at a time from 64 four-byte banks, i.e.
+// 256 bytes = four 64-byte rows per bank sweep. Piece c of row r is stored at
+// piece c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3: among any 16
+// consecutive rows the four rows sharing r % 4 get four different pieces, so
+// the 16 reads hit 16 different 16-byte bank groups (and any 8 consecutive
+// rows also spread over a 128-byte sweep).
+__device__ __forceinline__ constexpr int lds_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
 __device__ __forceinline__ uint32_t lds_off(int row, int piece) {
-  return static_cast<uint32_t>(row * 64 + ((piece ^ ((row >> 1) & 3)) << 4));
+  return static_cast<uint32_t>(row * 64 + ((piece ^ lds_swz(row)) << 4));
 }
 
 __device__ __forceinline__ void lds_store16(uint8_t* base, uint32_t off, u32x4_t v) {
@@ -110,6 +150,31 @@ __device__ __forceinline__ u32x4_t lds_frag(const uint8_t* tile, int row0, int k
 
 __device__ __forceinline__ u32x4_t gload16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// ------------------------------------------------------------------ LDS DMA
+// gfx950 global_load_lds_dwordx4: every lane fetches 16 bytes from its own
+// global address; the wave writes them to 1024 contiguous LDS bytes at
+// `lds_block` (wave-uniform), lane l at byte 16 * l. Counted by vmcnt.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, lds_block, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt = VM (0..63) and lgkmcnt = LGKM (0..15), expcnt free.
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies (that
+// fence waits for every outstanding load, which would drain the DMA pipeline).
+// Callers wait for their own loads with waitcnt<> first; the empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace twell

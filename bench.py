@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--workload", default="ffn1p5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
-    ap.add_argument("--only", choices=["forward", "gate", "fused", "dense", "copy"], default=None,
+    ap.add_argument("--only", choices=["forward", "gate", "fused", "fallback", "dense", "copy"], default=None,
                     help="run only this leg (for profiler runs); prints a short line")
     ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
     return ap.parse_args()
@@ -109,12 +109,13 @@ def main():
     y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     ws_fwd = tw.Workspace(dev)
-    ws_gate = tw.Workspace(dev)
+    ctrl_fwd = tw.Workspace(dev, zeroed=True)
+    ctrl_gate = tw.Workspace(dev, zeroed=True)
     ws_dense = tw.Workspace(dev)
     packed = tw.Packed.empty(w.M, w.F, w.T, w.C, dev)
 
-    fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_fwd)  # noqa: E731
-    gate = lambda: tw.gate_pack(x, Wg, w.T, w.C, out=packed, workspace=ws_gate)  # noqa: E731
+    fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_fwd, ctrl=ctrl_fwd)  # noqa: E731
+    gate = lambda: tw.gate_pack(x, Wg, w.T, w.C, out=packed, ctrl=ctrl_gate)  # noqa: E731
     fused = lambda: tw.fused_updown(x, WuT, Wd, packed, y=y)  # noqa: E731
     fallback = lambda: tw.dense_fallback(x, Wg, WuT, Wd, packed, y, workspace=ws_dense)  # noqa: E731
     y_dense = torch.empty_like(y)
@@ -123,11 +124,12 @@ def main():
     if args.only is not None:
         if args.only == "copy":
             n = args.copy_mb * (1 << 20) // 4
+            # a plain elementwise kernel of known traffic: reads and writes n floats
             src = torch.ones(n, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
-            fn = lambda: dst.copy_(src)  # noqa: E731
+            fn = lambda: torch.mul(src, 2.0, out=dst)  # noqa: E731
         else:
-            fn = {"forward": fwd, "gate": gate, "fused": fused, "dense": dense}[args.only]
+            fn = {"forward": fwd, "gate": gate, "fused": fused, "dense": dense, "fallback": fallback}[args.only]
             gate()  # the fused leg reads a packing
         for _ in range(args.warmup):
             fn()

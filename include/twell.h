@@ -26,11 +26,18 @@
  *    stream synchronisation. No exception crosses the ABI.
  *  - Shape limits: M >= 0 and M < 2^31; d % 256 == 0 and 256 <= d <= 8192;
  *    F > 0 with F % T == 0; T in {64, 128}; 1 <= C <= T.
- *  - Workspace: a caller-owned device buffer of at least
- *    twell_workspace_bytes(op, ...) bytes, 256-byte aligned. It MUST be
- *    zero-filled before its first use; every call leaves its control block
- *    zeroed again when it completes (in stream order). One workspace must not
- *    be used by two calls that may run concurrently.
+ *  - Workspace: a caller-owned device scratch buffer of at least
+ *    twell_workspace_bytes(op, ...) bytes, 256-byte aligned, contents
+ *    irrelevant. One workspace must not be used by two calls that may run
+ *    concurrently.
+ *  - Control block (twell_gate_pack, twell_ffn_forward): a caller-owned device
+ *    buffer of at least twell_ctrl_bytes(M) bytes, 256-byte aligned, used only
+ *    for this purpose. It must be zero-filled before its first use; every call
+ *    leaves it zero-filled again when it completes (stream order), so one
+ *    buffer sized for the largest M serves every later call. It holds the
+ *    overflow-set counters and one deduplication flag per row. Calls sharing a
+ *    control block must not run concurrently.
+ *  - With M == 0 nothing is computed; x and y may then be NULL.
  */
 #ifndef TWELL_H_
 #define TWELL_H_
@@ -48,7 +55,7 @@ extern "C" {
 #define TWELL_OK 0
 #define TWELL_E_INVALID_ARG (-1) /* null pointer, negative or zero dimension, M too large */
 #define TWELL_E_UNSUPPORTED (-2) /* F % T != 0, T not in {64,128}, C out of [1,T], d not supported */
-#define TWELL_E_WORKSPACE (-3)   /* workspace null, misaligned or smaller than required */
+#define TWELL_E_WORKSPACE (-3)   /* workspace or control block null, misaligned or too small */
 #define TWELL_E_HIP (-4)         /* a HIP launch failed (hipGetLastError) */
 
 /* Operations for twell_workspace_bytes. */
@@ -81,10 +88,10 @@ typedef struct twell_packed {
  * ReLU and the per-tile packing of `out`, in one launch and without writing z.
  * z_debug: optional [M, F] fp32; when non-NULL every pre-activation z is also
  * stored (for bit-exact checks of the packing), otherwise pass NULL.
- * workspace: >= twell_workspace_bytes(TWELL_OP_GATE_PACK, ...). */
+ * ctrl: control block of >= twell_ctrl_bytes(M) bytes (see above). */
 int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
                     int32_t T, int32_t C, const twell_packed* out, float* z_debug,
-                    void* workspace, size_t ws_bytes, void* stream);
+                    void* ctrl, size_t ctrl_bytes, void* stream);
 
 /* Fused up+down projection over a TwELL packing (tgviewer.app Telegram post,
  * part "Инференс"; aimodeling.com summary, paragraph 3): for every row that is
@@ -112,10 +119,11 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
 /* The whole sparse forward: twell_gate_pack, twell_fused_updown and
  * twell_dense_fallback on one stream, with the packing kept in the workspace
  * (see twell_packed_view). y [M, d] fp32 is fully written.
- * workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
+ * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                       const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
-                      float* y, void* workspace, size_t ws_bytes, void* stream);
+                      float* y, void* ctrl, size_t ctrl_bytes, void* workspace, size_t ws_bytes,
+                      void* stream);
 
 /* Dense MFMA gated-FFN baseline (the comparator the pages measure against:
  * dense matmuls, tgviewer.app Telegram post, paragraph after "Обучение"):
@@ -126,8 +134,12 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
                             void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs (0 for invalid arguments). T and C are
- * ignored for TWELL_OP_DENSE_FFN and TWELL_OP_DENSE_FALLBACK. */
+ * ignored for TWELL_OP_DENSE_FFN and TWELL_OP_DENSE_FALLBACK;
+ * TWELL_OP_GATE_PACK needs none (0 is a valid size for it). */
 size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C);
+
+/* Control-block bytes for up to M rows (0 for M < 0 or M too large). */
+size_t twell_ctrl_bytes(int64_t M);
 
 /* Where twell_ffn_forward keeps its packing inside `workspace` (host-side
  * pointer arithmetic only; nothing is enqueued). Valid after that call has

@@ -32,12 +32,13 @@ def test_abi_version_and_status_strings():
 @pytest.mark.parametrize("M,d,F,T,C", [(4096, 2048, 8192, 128, 16), (64, 256, 1024, 64, 8), (0, 256, 128, 64, 1)])
 def test_workspace_sizes(M, d, F, T, C):
     nT = F // T
-    g = tw.workspace_bytes(tw.OP_GATE_PACK, M, d, F, T, C)
+    g = tw.ctrl_bytes(M)
+    assert tw.workspace_bytes(tw.OP_GATE_PACK, M, d, F, T, C) == 0
     f = tw.workspace_bytes(tw.OP_FFN_FORWARD, M, d, F, T, C)
     dn = tw.workspace_bytes(tw.OP_DENSE_FFN, M, d, F)
     fb = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, M, d, F)
     assert g >= 256 + 4 * M and g % 256 == 0
-    assert f >= g + M * nT * C * 5 + M * nT * 2 + 4 * M + 4 * M * F
+    assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + 4 * M * F
     assert dn >= 2 * M * F and fb >= 4 * M * F
     assert f % 256 == 0 and dn % 256 == 0
 
@@ -64,31 +65,37 @@ def _packed():
 def test_gate_pack_validation():
     L = tw.lib()
     pk = _packed()
-    ok_ws = tw.workspace_bytes(tw.OP_GATE_PACK, 256, 256, 1024, 64, 8)
-    call = lambda *a: L.twell_gate_pack(*a)  # noqa: E731
-    assert call(None, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_ARG
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, None, None, FAKE, ok_ws, None) == E_ARG
+    cb = tw.ctrl_bytes(256)
+    assert cb >= 256 + 4 * 256 and tw.ctrl_bytes(-1) == 0
+    call = L.twell_gate_pack
+    assert call(None, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, cb, None) == E_ARG
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, None, None, FAKE, cb, None) == E_ARG
     bad = _Packed(FAKE.value, 0, FAKE.value, FAKE.value, FAKE.value)
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(bad), None, FAKE, ok_ws, None) == E_ARG
-    assert call(FAKE, FAKE, -5, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_ARG
-    assert call(FAKE, FAKE, 256, 256, 1000, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
-    assert call(FAKE, FAKE, 256, 256, 1024, 32, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 65, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
-    assert call(FAKE, FAKE, 256, 300, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws, None) == E_UNSUP
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, None, ok_ws, None) == E_WS
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, ok_ws - 1, None) == E_WS
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(bad), None, FAKE, cb, None) == E_ARG
+    no_n = _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, 0)
+    assert call(FAKE, FAKE, 0, 256, 1024, 64, 8, ctypes.byref(no_n), None, FAKE, cb, None) == E_ARG
+    assert call(FAKE, FAKE, -5, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, cb, None) == E_ARG
+    assert call(FAKE, FAKE, 256, 256, 1000, 64, 8, ctypes.byref(pk), None, FAKE, cb, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 32, 8, ctypes.byref(pk), None, FAKE, cb, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 65, ctypes.byref(pk), None, FAKE, cb, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 300, 1024, 64, 8, ctypes.byref(pk), None, FAKE, cb, None) == E_UNSUP
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, None, cb, None) == E_WS
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, cb - 1, None) == E_WS
     mis = ctypes.c_void_p(FAKE.value + 8)
-    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, mis, ok_ws, None) == E_WS
+    assert call(FAKE, FAKE, 256, 256, 1024, 64, 8, ctypes.byref(pk), None, mis, cb, None) == E_WS
 
 
 def test_forward_validation():
     L = tw.lib()
     ws = tw.workspace_bytes(tw.OP_FFN_FORWARD, 256, 256, 1024, 64, 8)
+    cb = tw.ctrl_bytes(256)
     f = L.twell_ffn_forward
-    assert f(FAKE, FAKE, None, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, ws, None) == E_ARG
-    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, None, FAKE, ws, None) == E_ARG
-    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 96, 8, FAKE, FAKE, ws, None) == E_UNSUP
-    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, ws - 256, None) == E_WS
+    assert f(FAKE, FAKE, None, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, None, FAKE, cb, FAKE, ws, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 96, 8, FAKE, FAKE, cb, FAKE, ws, None) == E_UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws - 256, None) == E_WS
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb - 4, FAKE, ws, None) == E_WS
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, None, cb, FAKE, ws, None) == E_WS
     d = L.twell_dense_ffn_forward
     dws = tw.workspace_bytes(tw.OP_DENSE_FFN, 256, 256, 1024)
     assert d(FAKE, FAKE, FAKE, FAKE, 256, 256, 1000, FAKE, FAKE, dws, None) == E_UNSUP
