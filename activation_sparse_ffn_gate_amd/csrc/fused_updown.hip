@@ -153,7 +153,11 @@ __global__ __launch_bounds__(256) void fused_updown_kernel(FusedArgs a) {
 
 template <int NCH>
 constexpr int unroll_for() {
-  return NCH <= 2 ? 8 : (NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1));
+#ifdef TWELL_FUSED_UNROLL
+  return TWELL_FUSED_UNROLL;
+#else
+  return NCH <= 2 ? 8 : (NCH <= 5 ? 4 : (NCH <= 8 ? 2 : 1));
+#endif
 }
 
 template <int VEC, int NCH>

@@ -41,7 +41,7 @@ constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kDmaPerStage = 8;  // global_load_lds per thread per stage (4 for A, 4 for B)
 
 template <int kT, bool kDebug>
-__global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m) {
+__global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m, int tiles_n) {
   // One LDS object only: with a second one the compiler attaches alias scopes
   // to LDS accesses and then makes every LDS read wait for all outstanding
   // DMA, which would drain the pipeline below.
@@ -53,12 +53,17 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
   const int wm = w >> 1, wn = w & 1;
 
   // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of tiles (token tiles fastest) so tiles that share a block
-  // of Wg rows run on the same L2.
+  // contiguous run of tile indices, and walk tiles in groups of 8 token tiles
+  // (unit tiles within a group), so the tiles an XCD runs at once form a
+  // compact block that shares x and Wg slices in its L2.
   const int nwg = gridDim.x, b = blockIdx.x;
   const int lin = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + (b / 8) : b;
-  const int m0 = (lin % tiles_m) * kBM;
-  const int n0 = (lin / tiles_m) * kBN;
+  constexpr int kGroupM = 8;
+  const int group = lin / (kGroupM * tiles_n);
+  const int gm = min(kGroupM, tiles_m - group * kGroupM);  // token tiles in this group
+  const int within = lin - group * kGroupM * tiles_n;
+  const int m0 = (group * kGroupM + within % gm) * kBM;
+  const int n0 = (within / gm) * kBN;
 
   // DMA addressing. A stage tile is 256 rows x 64 bytes; wave w fills the
   // 16-row blocks 4w .. 4w+3 of each operand. In a block, lane l lands on row
@@ -111,10 +116,13 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
     }
   };
   // One k step: the 16 MFMAs of `cur`; after each of the first 8 one fragment
-  // read of the next step (into `nxt`, buffer nbuf, half nks), after each of
-  // the last 8 one DMA of the batch for chunk dk0 (when kDma). The order is
-  // pinned so the matrix pipe is never idle behind an issue block.
-  auto step = [&](auto kDma, const Frags& cur, Frags& nxt, int nbuf, int nks, int dbuf, int dk0) {
+  // read of the next step (into `nxt`, buffer nbuf, half nks); after every
+  // other one of the last 8, one DMA (kDma0 .. kDma0 + 3, when kDma0 >= 0) of
+  // the batch for chunk dk0 into buffer dbuf. The order is pinned so the
+  // matrix pipe never waits behind an issue block, and each chunk's 32 DMAs
+  // per CU are spread over the whole chunk rather than queued at once.
+  auto step = [&](auto kDma0, const Frags& cur, Frags& nxt, int nbuf, int nks, int dbuf, int dk0) {
+    constexpr int d0 = decltype(kDma0)::value;
     const uint8_t* As = smem + nbuf * kStageBytes;
     const uint8_t* Bs = As + kTileBytes;
 #pragma unroll
@@ -124,8 +132,8 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
       if (i < 8) {
         if (i & 1) nxt.b[i >> 1] = lds_frag(Bs, wn * 128 + (i >> 1) * 32, nks, lane);
         else nxt.a[i >> 1] = lds_frag(As, wm * 128 + (i >> 1) * 32, nks, lane);
-      } else if constexpr (decltype(kDma)::value) {
-        dma(i - 8, dbuf, dk0);
+      } else if constexpr (d0 >= 0) {
+        if ((i & 1) == 0) dma(d0 + ((i - 8) >> 1), dbuf, dk0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -136,38 +144,48 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(f.a[mb], f.b[nb], acc[mb][nb]);
   };
-  constexpr std::true_type with_dma{};
-  constexpr std::false_type no_dma{};
+  constexpr std::integral_constant<int, -1> no_dma{};
+  constexpr std::integral_constant<int, 0> dma_lo{};  // DMAs 0-3 of a batch
+  constexpr std::integral_constant<int, 4> dma_hi{};  // DMAs 4-7 of a batch
 
   // Pipeline (nk >= 8 since d >= 256). Chunk kt's two k steps run from
   // registers f0 / f1 while the next step's fragments load. Halfway through
   // chunk kt every thread waits until its DMA of chunk kt + 1 has landed
-  // (later chunks may stay in flight); the barrier then publishes chunk
-  // kt + 1 and guarantees all waves are done with chunk kt - 1, whose buffer
-  // the DMA of chunk kt + kAhead reuses. Fragment reads never need waiting on
-  // at the barrier: the MFMAs that consumed them already waited.
+  // (chunks kt + 2 and kt + 3 may stay in flight); the barrier then publishes
+  // chunk kt + 1 and guarantees all waves are done with chunk kt - 1, whose
+  // buffer chunk kt + kAhead reuses: its DMAs 0-3 go out after this barrier,
+  // 4-7 in the first half of the next chunk (before the next wait). Fragment
+  // reads never need waiting on at the barrier: the MFMAs that consumed them
+  // already waited.
   const int nk = a.d / kBK;
-  // vmcnt allowing `chunks` later chunks (kDmaPerStage each) to stay in flight
+  // vmcnt allowing `chunks` later whole chunks (kDmaPerStage each) in flight
   auto wait_chunks = [](int chunks) {
-    if (chunks >= 3) waitcnt<3 * kDmaPerStage, 15>();
-    else if (chunks == 2) waitcnt<2 * kDmaPerStage, 15>();
+    if (chunks >= 2) waitcnt<2 * kDmaPerStage, 15>();
     else if (chunks == 1) waitcnt<kDmaPerStage, 15>();
     else waitcnt<0, 15>();
   };
+  static_assert(kAhead == 4, "the batch split below assumes chunks run four ahead");
 #pragma unroll
-  for (int s = 0; s < kAhead; ++s) issue(s, s * kBK);
-  wait_chunks(kAhead - 1);
+  for (int s = 0; s < kAhead - 1; ++s) issue(s, s * kBK);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma(j, kAhead - 1, (kAhead - 1) * kBK);  // chunk 3, first half
+  waitcnt<2 * kDmaPerStage + 4, 15>();  // chunk 0 landed
   raw_barrier();
   Frags f0, f1;
   load_frags(f0, 0, 0);
   int kt = 0;
-  for (; kt < nk - kAhead; ++kt) {  // steady state: a DMA batch every chunk
-    step(no_dma, f0, f1, kt % kStages, 1, 0, 0);
-    waitcnt<(kAhead - 2) * kDmaPerStage, 15>();
+  for (; kt < nk - kAhead; ++kt) {  // steady state
+    step(dma_hi, f0, f1, kt % kStages, 1, (kt + kAhead - 1) % kStages, (kt + kAhead - 1) * kBK);
+    waitcnt<2 * kDmaPerStage, 15>();
     raw_barrier();
-    step(with_dma, f1, f0, (kt + 1) % kStages, 0, (kt + kAhead) % kStages, (kt + kAhead) * kBK);
+    step(dma_lo, f1, f0, (kt + 1) % kStages, 0, (kt + kAhead) % kStages, (kt + kAhead) * kBK);
   }
-  for (; kt < nk - 1; ++kt) {  // drain: the last kAhead - 1 chunk boundaries
+  // first drain iteration still completes the last chunk's batch
+  step(dma_hi, f0, f1, kt % kStages, 1, (kt + kAhead - 1) % kStages, (kt + kAhead - 1) * kBK);
+  wait_chunks(nk - 2 - kt);
+  raw_barrier();
+  step(no_dma, f1, f0, (kt + 1) % kStages, 0, 0, 0);
+  for (++kt; kt < nk - 1; ++kt) {
     step(no_dma, f0, f1, kt % kStages, 1, 0, 0);
     wait_chunks(nk - 2 - kt);
     raw_barrier();
@@ -329,11 +347,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   const dim3 grid(tiles_m * tiles_n), block(256);
   const bool dbg = a.z_debug != nullptr;
   if (a.T == 128) {
-    if (dbg) gate_pack_kernel<128, true><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_kernel<128, false><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_kernel<128, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else gate_pack_kernel<128, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
   } else {
-    if (dbg) gate_pack_kernel<64, true><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_kernel<64, false><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_kernel<64, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else gate_pack_kernel<64, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
