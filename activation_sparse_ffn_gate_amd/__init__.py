@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     OP_DENSE_FFN,
     OP_FFN_FORWARD,
     OP_GATE_PACK,
+    OP_SLICED_UPDOWN,
     LIB_PATH,
     Packed,
     TwellError,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     packed_view,
+    sliced_updown,
     status_string,
     workspace_bytes,
 )

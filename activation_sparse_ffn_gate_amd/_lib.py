@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libtwell.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "twell.h")
 
 TWELL_OK = 0
-OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK = 0, 1, 2, 3
+OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK, OP_SLICED_UPDOWN = 0, 1, 2, 3, 4
 
 
 class TwellError(RuntimeError):
@@ -42,6 +42,7 @@ _PK = ctypes.POINTER(_Packed)
 _SIGNATURES = {
     "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
     "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
+    "twell_sliced_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
@@ -235,6 +236,19 @@ def fused_updown(x, WuT, Wd, packed: Packed, y=None):
     pk = packed._c()
     _check(lib().twell_fused_updown(*args, ctypes.byref(pk), M, d, F, packed.T, packed.C, _dptr(y), _stream(x)),
            "twell_fused_updown")
+    return y
+
+
+def sliced_updown(x, WuT, Wd, packed: Packed, y=None, workspace=None):
+    M, d = x.shape
+    F = WuT.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_SLICED_UPDOWN, M, d, F, packed.T, packed.C))
+    pk = packed._c()
+    _check(lib().twell_sliced_updown(*args, ctypes.byref(pk), M, d, F, packed.T, packed.C, _dptr(y), wp, wn,
+                                     _stream(x)), "twell_sliced_updown")
     return y
 
 

@@ -1,0 +1,376 @@
+// Up + down projections over a TwELL packing, split by model-dimension slice
+// so that every XCD's weight gathers stay in its own L2 (gfx950).
+//
+// What is computed is the fused kernel's operation (Telegram post on TwELL at
+// tgviewer.app, part "Инференс"; aimodeling.com summary, paragraph 3): for
+// each stored unit j of a row, u_j = x_r . WuT[j], h_j = g_j * u_j, and
+// y_r = sum_j h_j * Wd[j]. The difference is where the bytes come from.
+//
+// MI355X has 8 XCDs, each with its own 4 MB L2, and workgroups are dispatched
+// to the XCDs round-robin, so blockIdx % 8 names the XCD a workgroup runs on.
+// The one-wave-per-token kernel gathers whole 2d-byte rows of WuT and Wd from
+// every XCD, so the gathers miss L2 and run at the HBM/MALL rate. Here the d
+// columns are cut into 8 slices and the workgroups of XCD k only touch slice k
+// of WuT and Wd: F * (d / 8) * 2 bytes per matrix (4 MB at F = 8192,
+// d = 2048), which that XCD's L2 can hold, so the repeated per-unit gathers
+// become L2 hits.
+//
+// The price is one exchange between the slices, since u_j needs all d
+// columns. Two launches:
+//   up:   wave per (row, slice s): part[s][r][e] = g_e * (x_r[s] . WuT[j_e][s])
+//         for the e-th stored unit of the row (tile-major, slot order);
+//   down: wave per (row, slice s): h_e = sum over s' of part[s'][r][e] in the
+//         fixed order s' = 0..7, y_r[s] = sum_e h_e * Wd[j_e][s].
+// So a stored unit's hidden value does pass through memory: 8 fp32 partials per
+// stored unit (the dense hidden matrix is still never formed). part is laid
+// out [8][M][nT * C] so each row's partials of a slice are contiguous. The up
+// pass also leaves each row's unit list (units [M][nT * C]) and its length
+// (row_len [M], -1 for an overflow row), so the down pass starts from those
+// instead of re-reading counts and indices.
+//
+// Lane layout. A slice is d / 8 bf16 = d / 64 sixteen-byte pieces. A row of a
+// slice is read by a group of L lanes (L = the largest power of two <= 64
+// dividing d / 64), each lane holding V = (d / 64) / L pieces, so one load
+// instruction of the wave reads G = 64 / L different stored units, each
+// group's lanes covering 16 * L contiguous bytes. The up pass reduces within
+// the group; the down pass keeps G partial output slices and sums them across
+// groups once at the end. Overflow rows (some count > C) are skipped, as in the
+// fused kernel; the dense fallback writes them.
+#include "twell_device.hpp"
+#include "twell_internal.hpp"
+
+namespace twell {
+namespace {
+
+constexpr int kRowsPerWG = 4;      // one wave per (row, slice)
+constexpr int kListCap = 256;       // stored units staged per wave per round
+constexpr int kCountGroups = 2;     // rows of up to 128 tiles keep their counts in registers
+
+// Sum over aligned groups of L lanes; every lane of a group gets the sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror: other quad of the 8
+  if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror: other 8 of the 16
+  if constexpr (L >= 32) v += xor_lanes<16>(v);
+  if constexpr (L >= 64) v = sum_halves(v);
+  return v;
+}
+
+// Stages the stored units of one row into LDS in (tile, slot) order, kListCap
+// at a time, and runs body(n, e0) with units e0 .. e0 + n - 1 staged (unit
+// index lj[i] and, if kWithValues, gate value lg[i]). Counts of the first
+// 64 * kCountGroups tiles come in `c` (lane l: tile 64 q + l); the usual case,
+// a row with at most that many tiles and kListCap units, is staged in one
+// round. Returns the row's number of stored units.
+template <bool kWithValues, class Body>
+__device__ __forceinline__ int stage_row(const SlicedArgs& a, int row, const int (&c)[kCountGroups],
+                                         int* lj, float* lg, Body&& body) {
+  const int lane = threadIdx.x & 63;
+  const int nT = a.F / a.T;
+  const int C = a.C;
+  const int tmask = a.T - 1;  // T is a power of two: keeps every unit index < F
+  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
+
+  int off[kCountGroups];
+  int total = 0;
+#pragma unroll
+  for (int q = 0; q < kCountGroups; ++q) {
+    off[q] = 0;
+    if (q * 64 < nT) {  // uniform
+      const int incl = wave_inclusive_scan(c[q]);
+      off[q] = total + incl - c[q];
+      total += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  if (nT <= 64 * kCountGroups && total <= kListCap) {
+#pragma unroll
+    for (int q = 0; q < kCountGroups; ++q) {
+      const int t = q * 64 + lane;
+      const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
+      for (int s = 0; s < c[q]; ++s) {
+        lj[off[q] + s] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
+        if constexpr (kWithValues) lg[off[q] + s] = a.vals[slot0 + s];
+      }
+    }
+    wave_lds_sync();
+    if (total > 0) body(total, 0);
+    wave_lds_sync();
+    return total;
+  }
+
+  // General case: tile groups of 64 one after another, kListCap units a round.
+  int ebase = 0;
+  for (int t0 = 0; t0 < nT; t0 += 64) {
+    const int t = t0 + lane;
+    const int ct = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
+    const int incl = wave_inclusive_scan(ct);
+    const int gtotal = __builtin_amdgcn_readlane(incl, 63);
+    const int o = incl - ct;
+    const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
+    for (int base = 0; base < gtotal; base += kListCap) {
+      const int s_lo = max(0, base - o);
+      const int s_hi = min(ct, base + kListCap - o);
+      for (int s = s_lo; s < s_hi; ++s) {
+        lj[o + s - base] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
+        if constexpr (kWithValues) lg[o + s - base] = a.vals[slot0 + s];
+      }
+      wave_lds_sync();
+      body(min(kListCap, gtotal - base), ebase + base);
+      wave_lds_sync();
+    }
+    ebase += gtotal;
+  }
+  return ebase;
+}
+
+template <int L, int V, int U>
+__global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
+  constexpr int G = 64 / L;
+  __shared__ int s_j[kRowsPerWG][kListCap];
+  __shared__ float s_g[kRowsPerWG][kListCap];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slice = blockIdx.x % kSlices;
+  const int row = (blockIdx.x / kSlices) * kRowsPerWG + w;
+  if (row >= a.M) return;
+
+  const int nT = a.F / a.T;
+  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
+  int c[kCountGroups];
+  bool over = false;
+#pragma unroll
+  for (int q = 0; q < kCountGroups; ++q) {
+    const int t = q * 64 + lane;
+    c[q] = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
+    over |= c[q] > a.C;
+  }
+  for (int t = 64 * kCountGroups + lane; t < nT; t += 64) over |= cnt_row[t] > a.C;
+  if (__ballot(over) != 0) {  // owned by the dense fallback
+    if (slice == 0 && lane == 0) a.row_len[row] = -1;
+    return;
+  }
+
+  const int grp = lane / L, li = lane % L;
+  const int col0 = slice * (a.d / kSlices) + li * 8;  // piece v of this lane: col0 + v * 8L
+  u32x4_t xv[V];
+  const uint16_t* xr = a.x + static_cast<size_t>(row) * a.d + col0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) xv[v] = gload16(xr + v * 8 * L);
+
+  const size_t cap = static_cast<size_t>(nT) * a.C;
+  float* prow = a.part + (static_cast<size_t>(slice) * a.M + row) * cap;
+  int32_t* urow = a.units + static_cast<size_t>(row) * cap;
+  int* lj = s_j[w];
+  float* lg = s_g[w];
+
+  const int total = stage_row<true>(a, row, c, lj, lg, [&](int n, int e0) {
+    if (slice == 0)  // the row's unit list, for the down pass
+      for (int i = lane; i < n; i += 64) urow[e0 + i] = lj[i];
+    for (int e = 0; e < n; e += G * U) {
+      u32x4_t wu[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = lj[min(e + u * G + grp, n - 1)];
+        const uint16_t* p = a.WuT + static_cast<size_t>(j) * a.d + col0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) wu[u][v] = gload16(p + v * 8 * L);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float part = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) part = dot2_bf16(xv[v][q], wu[u][v][q], part);
+        part = group_sum<L>(part);
+        const int k = e + u * G + grp;
+        if (li == 0 && k < n) prow[e0 + k] = lg[k] * part;
+      }
+    }
+  });
+  if (slice == 0 && lane == 0) a.row_len[row] = total;
+}
+
+// L > 32 (one group, lanes >= L idle) avoids the cross-group sum for the
+// slice widths that are not a power-of-two number of pieces.
+template <int L, int V, int U>
+__global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
+  constexpr int G = 64 / L;
+  __shared__ int s_j[kRowsPerWG][kListCap];
+  __shared__ float s_h[kRowsPerWG][kListCap];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slice = blockIdx.x % kSlices;
+  const int row = (blockIdx.x / kSlices) * kRowsPerWG + w;
+  if (row >= a.M) return;
+  const int n = __builtin_amdgcn_readfirstlane(a.row_len[row]);
+  if (n < 0) return;  // overflow row
+
+  const int grp = (G == 1) ? 0 : lane / L;
+  const int li = (G == 1) ? min(lane, L - 1) : lane % L;  // idle lanes repeat the last piece
+  const int col0 = slice * (a.d / kSlices) + li * 8;
+  const size_t cap = static_cast<size_t>(a.F / a.T) * a.C;
+  const size_t slice_stride = static_cast<size_t>(a.M) * cap;
+  const float* prow = a.part + static_cast<size_t>(row) * cap;
+  const int32_t* urow = a.units + static_cast<size_t>(row) * cap;
+  int* lj = s_j[w];
+  float* lh = s_h[w];
+
+  float acc[V][8];
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[v][k] = 0.f;
+
+  for (int e0 = 0; e0 < n; e0 += kListCap) {
+    const int m = min(kListCap, n - e0);
+    // unit index and h of the staged units: the slices' partial products summed
+    // in slice order
+    for (int i = lane; i < m; i += 64) {
+      lj[i] = urow[e0 + i];
+      float h = 0.f;
+#pragma unroll
+      for (int s = 0; s < kSlices; ++s) h += prow[s * slice_stride + e0 + i];
+      lh[i] = h;
+    }
+    wave_lds_sync();
+    for (int e = 0; e < m; e += G * U) {
+      u32x4_t wd[U][V];
+      float hv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = e + u * G + grp;
+        const int j = lj[min(k, m - 1)];
+        hv[u] = (k < m) ? lh[k] : 0.f;
+        const uint16_t* p = a.Wd + static_cast<size_t>(j) * a.d + col0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) wd[u][v] = gload16(p + v * 8 * L);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[v][2 * q] = fmaf(hv[u], bf16_lo(wd[u][v][q]), acc[v][2 * q]);
+            acc[v][2 * q + 1] = fmaf(hv[u], bf16_hi(wd[u][v][q]), acc[v][2 * q + 1]);
+          }
+    }
+    wave_lds_sync();
+  }
+
+  // The G groups hold partial sums of the same output columns.
+  static_for<0, 6>([&](auto I) {
+    constexpr int X = 1 << I.value;
+    if constexpr (X >= L && X < 64) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if constexpr (X == 32)
+            acc[v][k] = sum_halves(acc[v][k]);
+          else
+            acc[v][k] += xor_lanes<X>(acc[v][k]);
+        }
+    }
+  });
+
+  float* yr = a.y + static_cast<size_t>(row) * a.d + col0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if (v % G == grp && (G > 1 || lane < L)) {
+      *reinterpret_cast<float4*>(yr + v * 8 * L) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+      *reinterpret_cast<float4*>(yr + v * 8 * L + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+    }
+  }
+}
+
+// Loads in flight per lane per step: about 4 sixteen-byte vectors (deeper
+// unrolling costs more in occupancy than it gains).
+template <int V>
+constexpr int unroll_for() {
+  return V <= 1 ? 4 : (V <= 2 ? 2 : 1);
+}
+
+template <int L, int V>
+hipError_t launch_up(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
+  sliced_up_kernel<L, V, unroll_for<V>()><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int L, int V>
+hipError_t launch_down(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
+  sliced_down_kernel<L, V, unroll_for<V>()><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// pieces = d / 64 sixteen-byte pieces per slice row. Up pass: L = the largest
+// power of two <= 64 dividing pieces, V = pieces / L. Down pass: the same,
+// except that 32 < pieces < 64 uses one group of `pieces` lanes (V = 1).
+bool lane_split(int d, bool down, int* L, int* V) {
+  if (d < 256 || d > 8192 || d % 256 != 0) return false;
+  const int pieces = d / 64;
+  if (down && pieces > 32 && pieces < 64) {
+    *L = pieces;
+    *V = 1;
+    return true;
+  }
+  int l = 64;
+  while (pieces % l != 0) l >>= 1;
+  *L = l;
+  *V = pieces / l;
+  return *V <= 7;
+}
+
+// Instantiated (L, V) pairs; the switch key is L * 8 + V.
+#define TWELL_SLICED_SHAPES(X)                                                                   \
+  X(64, 1) X(64, 2) X(32, 1) X(32, 3) X(16, 1) X(16, 3) X(16, 5) X(16, 7) X(8, 1) X(8, 3) X(8, 5) \
+      X(8, 7) X(4, 1) X(4, 3) X(4, 5) X(4, 7)
+#define TWELL_WIDE_DOWN_SHAPES(X) X(40, 1) X(48, 1) X(56, 1)
+
+}  // namespace
+
+bool sliced_supports_d(int d) {
+  int L, V;
+  return lane_split(d, false, &L, &V) && lane_split(d, true, &L, &V);
+}
+
+SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C) {
+  const size_t cap = size_t(F / T) * size_t(C);
+  SlicedLayout l;
+  l.part = 0;
+  l.units = align256(size_t(kSlices) * size_t(M) * cap * sizeof(float));
+  l.row_len = l.units + align256(size_t(M) * cap * sizeof(int32_t));
+  l.total = l.row_len + align256(size_t(M) * sizeof(int32_t));
+  return l;
+}
+
+hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s) {
+  int Lu, Vu, Ld, Vd;
+  if (!lane_split(a.d, false, &Lu, &Vu) || !lane_split(a.d, true, &Ld, &Vd)) return hipErrorInvalidValue;
+  const dim3 grid(((a.M + kRowsPerWG - 1) / kRowsPerWG) * kSlices), block(64 * kRowsPerWG);
+  hipError_t e = hipErrorInvalidValue;
+  switch (Lu * 8 + Vu) {
+#define TWELL_CASE(L, V) \
+  case L * 8 + V: e = launch_up<L, V>(a, s, grid, block); break;
+    TWELL_SLICED_SHAPES(TWELL_CASE)
+#undef TWELL_CASE
+    default: break;
+  }
+  if (e != hipSuccess) return e;
+  e = hipErrorInvalidValue;
+  switch (Ld * 8 + Vd) {
+#define TWELL_CASE(L, V) \
+  case L * 8 + V: e = launch_down<L, V>(a, s, grid, block); break;
+    TWELL_SLICED_SHAPES(TWELL_CASE) TWELL_WIDE_DOWN_SHAPES(TWELL_CASE)
+#undef TWELL_CASE
+    default: break;
+  }
+  return e;
+}
+
+}  // namespace twell

@@ -2,6 +2,8 @@
 // and launch order. Declared and documented in include/twell.h.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/twell.h"
 #include "twell_internal.hpp"
 
@@ -13,7 +15,7 @@ constexpr int64_t kMaxM = int64_t(1) << 30;
 constexpr int64_t kMaxF = int64_t(1) << 24;
 
 struct Layout {
-  size_t vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0;
+  size_t vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0, part = 0;
   size_t total = 0;
 };
 
@@ -33,14 +35,23 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
   switch (op) {
     case TWELL_OP_GATE_PACK:
       break;
-    case TWELL_OP_FFN_FORWARD:
+    case TWELL_OP_FFN_FORWARD: {
       L.vals = take(m * nT * size_t(C) * 4);
       L.idx = take(m * nT * size_t(C));
       L.counts = take(m * nT * 2);
       L.ovf_rows = take(m * 4);
       L.n_ovf = take(4);
-      L.h_hi = take(m * f * 2);
-      L.h_lo = take(m * f * 2);
+      // The up/down partials and the fallback's hidden pair are live at
+      // different times of the stream, so they share one region.
+      const size_t h_bytes = align256(m * f * 2);
+      const size_t scratch = take(std::max(2 * h_bytes, twell::sliced_layout(M, F, T, C).total));
+      L.part = scratch;
+      L.h_hi = scratch;
+      L.h_lo = scratch + h_bytes;
+      break;
+    }
+    case TWELL_OP_SLICED_UPDOWN:
+      L.part = take(twell::sliced_layout(M, F, T, C).total);
       break;
     case TWELL_OP_DENSE_FFN:
       L.h_hi = take(m * f * 2);
@@ -147,6 +158,31 @@ int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const
   return hip_status(twell::launch_fused_updown(a, s));
 }
 
+// `region` is the sliced kernels' workspace region (twell::sliced_layout).
+int sliced_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
+                int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, void* region, float* y,
+                hipStream_t s) {
+  if (M == 0) return TWELL_OK;
+  const twell::SlicedLayout sl = twell::sliced_layout(M, F, T, C);
+  twell::SlicedArgs a;
+  a.x = x;
+  a.WuT = WuT;
+  a.Wd = Wd;
+  a.vals = in->vals;
+  a.idx = in->idx;
+  a.counts = in->counts;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.part = at<float>(region, sl.part);
+  a.units = at<int32_t>(region, sl.units);
+  a.row_len = at<int32_t>(region, sl.row_len);
+  a.y = y;
+  return hip_status(twell::launch_sliced_updown(a, s));
+}
+
 int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
                int64_t M, int64_t d, int64_t F, const int32_t* rows, const int32_t* n_rows,
                uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s) {
@@ -194,6 +230,21 @@ int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* W
   return fused_impl(x, WuT, Wd, in, M, d, F, T, C, y, static_cast<hipStream_t>(stream));
 }
 
+int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
+                        const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                        int32_t C, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!WuT || !Wd || !in) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!x || !y || !in->vals || !in->idx || !in->counts)) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK && !twell::sliced_supports_d(int(d))) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_SLICED_UPDOWN, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  const Layout L = layout(TWELL_OP_SLICED_UPDOWN, M, F, T, C);
+  return sliced_impl(x, WuT, Wd, in, M, d, F, T, C, at<uint8_t>(workspace, L.part), y,
+                     static_cast<hipStream_t>(stream));
+}
+
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                          const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
                          int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream) {
@@ -224,7 +275,10 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   const twell_packed p = packed_in_ws(workspace, L);
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
-  st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
+  if (twell::sliced_supports_d(int(d)))
+    st = sliced_impl(x, WuT, Wd, &p, M, d, F, T, C, at<uint8_t>(workspace, L.part), y, s);
+  else
+    st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
   if (st != TWELL_OK) return st;
   return dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                     at<uint16_t>(workspace, L.h_lo), y, s);
@@ -245,8 +299,9 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
 
 size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
   if (check_dims(M, d, F) != TWELL_OK) return 0;
-  if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD) {
+  if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD || op == TWELL_OP_SLICED_UPDOWN) {
     if (check_tc(F, T, C) != TWELL_OK) return 0;
+    if (op == TWELL_OP_SLICED_UPDOWN && !twell::sliced_supports_d(int(d))) return 0;
   } else if (op == TWELL_OP_DENSE_FFN || op == TWELL_OP_DENSE_FALLBACK) {
     if (F % 64 != 0) return 0;
     T = 0;

@@ -102,6 +102,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Value held by lane (this lane ^ X), X in 1..16 (ds_swizzle bit mode, which
+// permutes within each 32 lanes).
+template <int X>
+__device__ __forceinline__ float xor_lanes(float v) {
+  static_assert(X >= 1 && X <= 16, "xor within 32 lanes");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (X << 10) | 0x1F));
+}
+
+// v[l] + v[l ^ 32] on every lane l (v_permlane32_swap exchanges the two
+// halves); both lanes of a pair add the same operands in the same order.
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 // Inclusive prefix sum over the lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -52,7 +52,32 @@ struct DenseArgs {
   float* y;
 };
 
+// Up + down projections split into kSlices column slices of d, one per XCD.
+constexpr int kSlices = 8;
+
+struct SlicedArgs {
+  const uint16_t* x;
+  const uint16_t* WuT;
+  const uint16_t* Wd;
+  const float* vals;
+  const uint8_t* idx;
+  const uint16_t* counts;
+  int M, d, F, T, C;
+  float* part;       // [kSlices, M, (F / T) * C] partial up-projections
+  int32_t* units;    // [M, (F / T) * C] each row's stored units in (tile, slot) order
+  int32_t* row_len;  // [M] number of stored units, -1 for an overflow row
+  float* y;
+};
+
+// Byte offsets of the sliced kernels' buffers inside their workspace region.
+struct SlicedLayout {
+  size_t part, units, row_len, total;
+};
+
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
+bool sliced_supports_d(int d);
+SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
 hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);

@@ -84,7 +84,8 @@ def parse():
     ap.add_argument("--workload", default="ffn1p5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
-    ap.add_argument("--only", choices=["forward", "gate", "fused", "fallback", "dense", "copy"], default=None,
+    ap.add_argument("--only", choices=["forward", "gate", "fused", "sliced", "fallback", "dense", "copy"],
+                    default=None,
                     help="run only this leg (for profiler runs); prints a short line")
     ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
@@ -171,6 +172,9 @@ def main():
     fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_fwd, ctrl=ctrl_fwd)  # noqa: E731
     gate = lambda: tw.gate_pack(x, Wg, w.T, w.C, out=packed, ctrl=ctrl_gate)  # noqa: E731
     fused = lambda: tw.fused_updown(x, WuT, Wd, packed, y=y)  # noqa: E731
+    ws_sliced = tw.Workspace(dev)
+    sliced_ok = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, w.M, w.d, w.F, w.T, w.C) > 0
+    sliced = lambda: tw.sliced_updown(x, WuT, Wd, packed, y=y, workspace=ws_sliced)  # noqa: E731
     fallback = lambda: tw.dense_fallback(x, Wg, WuT, Wd, packed, y, workspace=ws_dense)  # noqa: E731
     y_dense = torch.empty_like(y)
     dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y_dense, workspace=ws_dense)  # noqa: E731
@@ -183,7 +187,8 @@ def main():
             dst = torch.empty_like(src)
             fn = lambda: torch.mul(src, 2.0, out=dst)  # noqa: E731
         else:
-            fn = {"forward": fwd, "gate": gate, "fused": fused, "dense": dense, "fallback": fallback}[args.only]
+            fn = {"forward": fwd, "gate": gate, "fused": fused, "sliced": sliced, "dense": dense,
+                  "fallback": fallback}[args.only]
             gate()  # the fused leg reads a packing
         for _ in range(args.warmup):
             fn()
@@ -213,13 +218,18 @@ def main():
     nnz_fit = int(counts[fit].sum())
     nnz_all = int(counts.sum())
     k_steps = max(args.steps, 20)
-    for fn in (gate, fused, fallback, dense):
+    legs = [gate, fused, fallback, dense] + ([sliced] if sliced_ok else [])
+    for fn in legs:
         fn()
     torch.cuda.synchronize()
     t_gate = time_loop(gate, k_steps, stream)
     t_fused = time_loop(fused, k_steps, stream)
+    t_sliced = time_loop(sliced, k_steps, stream) if sliced_ok else None
     t_fb = time_loop(fallback, k_steps, stream)
     t_dense = time_loop(dense, k_steps, stream)
+    # the up/down form twell_ffn_forward runs
+    t_updown = t_sliced if sliced_ok else t_fused
+    updown_name = "sliced_updown" if sliced_ok else "fused_updown"
 
     nT = w.F // w.T
     gate_flops = 2.0 * w.M * w.d * w.F
@@ -229,17 +239,18 @@ def main():
     fused_bytes = nnz_fit * 4.0 * w.d + fit.sum() * (2.0 * w.d + 4.0 * w.d) + w.M * 2.0 * nT + nnz_fit * 5.0
     gate_tflops = gate_flops / (t_gate * 1e-3) / 1e12
     fused_gbs = fused_bytes / (t_fused * 1e-3) / 1e9
+    updown_gbs = fused_bytes / (t_updown * 1e-3) / 1e9
     traffic = None  # HBM-side bytes per launch from the recorded counters, if still current
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
         if rec.get("sources_sha256") == sources_hash():
             ent = rec.get("workloads", {}).get(args.workload, {})
-            kern = ent.get("fused_updown" if t_fused >= t_gate else "gate_pack")
+            kern = ent.get(updown_name if t_updown >= t_gate else "gate_pack")
             traffic = round(kern["traffic_bytes"]) if kern else None
-    if t_fused >= t_gate:
-        roof = {"kernel": "fused_updown", "bound": "hbm", "achieved": round(fused_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(fused_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    if t_updown >= t_gate:
+        roof = {"kernel": updown_name, "bound": "hbm", "achieved": round(updown_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(updown_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(gate_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
@@ -267,6 +278,9 @@ def main():
             "fused_updown_ms": round(t_fused, 5),
             "fused_updown_gbs": round(fused_gbs, 1),
             "fused_updown_hbm_frac": round(fused_gbs / PEAK_HBM_GBS, 4),
+            "sliced_updown_ms": round(t_sliced, 5) if sliced_ok else None,
+            "sliced_updown_gbs": round(updown_gbs, 1) if sliced_ok else None,
+            "forward_updown": updown_name,
             "dense_fallback_ms": round(t_fb, 5),
             "nnz_per_token": round(nnz_all / w.M, 3),
             "overflow_rows": n_ovf,

@@ -63,6 +63,7 @@ extern "C" {
 #define TWELL_OP_FFN_FORWARD 1
 #define TWELL_OP_DENSE_FFN 2
 #define TWELL_OP_DENSE_FALLBACK 3
+#define TWELL_OP_SLICED_UPDOWN 4
 
 /* TwELL packing of ReLU(x Wg^T) with tile width T and capacity C
  * (the format: tgviewer.app Telegram post, part "Вот тут и решает TwELL";
@@ -104,6 +105,24 @@ int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* W
                        const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
                        int32_t C, float* y, void* stream);
 
+/* The operation of twell_fused_updown, computed for MI355X's 8 XCDs: the d
+ * columns are cut into 8 slices and the workgroups of XCD k gather only slice k
+ * of WuT and Wd, F * d / 8 bf16 per matrix, which stays in that XCD's L2
+ * (which rows are gathered and what is summed are as in the pages' inference
+ * kernel: tgviewer.app Telegram post, part "Инференс"; aimodeling.com summary,
+ * paragraph 3). Two launches: the first stores, per stored unit and slice,
+ * g_j * (x_r . WuT[j]) over that slice's columns; the second sums the 8
+ * partials of each unit in slice order and accumulates h_j * Wd[j] over its
+ * slice. Same contract for y as twell_fused_updown (overflow rows untouched).
+ * workspace: >= twell_workspace_bytes(TWELL_OP_SLICED_UPDOWN, ...)
+ * = 8 * M * (F / T) * C fp32 partials.
+ * d must be one of 256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072,
+ * 3584, 4096, 5120, 6144, 7168, 8192 (d / 64 = 2^a * b with b in {1, 3, 5, 7}),
+ * otherwise TWELL_E_UNSUPPORTED. */
+int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
+                        const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                        int32_t C, float* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* Dense fallback for the overflow rows of a packing (rows that do not fit the
  * sparse block go to a dense path: tgviewer.app Telegram post, part
  * "Обучение"; Tencent Cloud article, section 3). For the *in->n_ovf rows listed
@@ -116,8 +135,9 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
                          const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
                          int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream);
 
-/* The whole sparse forward: twell_gate_pack, twell_fused_updown and
- * twell_dense_fallback on one stream, with the packing kept in the workspace
+/* The whole sparse forward: twell_gate_pack, then twell_sliced_updown (or
+ * twell_fused_updown for the d that the sliced form does not support), then
+ * twell_dense_fallback, on one stream, with the packing kept in the workspace
  * (see twell_packed_view). y [M, d] fp32 is fully written.
  * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,

@@ -41,6 +41,19 @@ def test_workspace_sizes(M, d, F, T, C):
     assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + 4 * M * F
     assert dn >= 2 * M * F and fb >= 4 * M * F
     assert f % 256 == 0 and dn % 256 == 0
+    sl = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, M, d, F, T, C)
+    assert sl >= 8 * M * nT * C * 4 and sl % 256 == 0
+    # the forward's scratch holds either the sliced partials or the fallback's hidden pair
+    assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + max(sl - 256, 4 * M * F)
+
+
+@pytest.mark.parametrize("d,ok", [(256, True), (768, True), (2048, True), (2560, True), (4096, True),
+                                  (7168, True), (8192, True), (2304, False), (4608, False), (7936, False)])
+def test_sliced_supported_d(d, ok):
+    """d / 64 must be 2^a * b with b in {1, 3, 5, 7} (b <= 2 at 2^a = 64)."""
+    n = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, 64, d, 1024, 64, 8)
+    assert (n > 0) == ok
+    assert tw.workspace_bytes(tw.OP_FFN_FORWARD, 64, d, 1024, 64, 8) > 0  # the fused form covers the rest
 
 
 @pytest.mark.parametrize(
@@ -104,6 +117,13 @@ def test_forward_validation():
     pk = _packed()
     assert u(FAKE, FAKE, FAKE, None, 256, 256, 1024, 64, 8, FAKE, None) == E_ARG
     assert u(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 0, FAKE, None) == E_UNSUP
+    sl = L.twell_sliced_updown
+    sws = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, 256, 256, 1024, 64, 8)
+    assert sl(FAKE, FAKE, FAKE, None, 256, 256, 1024, 64, 8, FAKE, FAKE, sws, None) == E_ARG
+    assert sl(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 0, FAKE, FAKE, sws, None) == E_UNSUP
+    assert sl(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 2304, 1024, 64, 8, FAKE, FAKE, sws, None) == E_UNSUP
+    assert sl(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 8, FAKE, FAKE, sws - 1, None) == E_WS
+    assert sl(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 8, FAKE, None, sws, None) == E_WS
     fb = L.twell_dense_fallback
     fws = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, 256, 256, 1024)
     assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, FAKE, fws - 1, None) == E_WS

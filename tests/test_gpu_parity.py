@@ -42,6 +42,11 @@ SMALL = {
     "zipf_small": scaled(WORKLOADS["ffn2b_zipf"], M=520, d=768, F=1280, T=64, C=8, mean_nnz=20.0),
     "t64_odd_tiles": scaled(WORKLOADS["tiny"], M=130, d=512, F=192, T=64, C=4),
     "dense11_small": scaled(WORKLOADS["sweep_p11pct"], M=257, d=512, F=1024),
+    # ~900 stored units per row, 128 tiles of capacity T: never overflows, and
+    # every row's list spans several LDS rounds and tile groups of both kernels
+    "long_rows": scaled(WORKLOADS["sweep_p11pct"], M=96, d=512, F=8192, T=64, C=64),
+    # d = 2304 is not one the sliced kernels take: the forward uses the fused one
+    "fused_only_d2304": scaled(WORKLOADS["ffn1p5b"], M=200, d=2304, F=1024, mean_nnz=12.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith("sweep_")
@@ -99,10 +104,15 @@ def test_forward_matches_definition(name):
     print(f"{name}: rel L2 {rel:.2e}, max abs {mx:.2e}")
 
 
+def sliced_ok(d):
+    return tw.workspace_bytes(tw.OP_SLICED_UPDOWN, 1, d, 1024, 64, 8) > 0
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_components_compose(name):
-    """gate_pack + fused_updown + dense_fallback == ffn_forward, bit for bit;
-    fused_updown leaves overflow rows alone; packed_view shows the packing."""
+    """gate_pack + (sliced or fused) up/down + dense_fallback == ffn_forward,
+    bit for bit; the up/down kernels leave overflow rows alone; packed_view
+    shows the packing."""
     inp, _, _, _ = small_case(name)
     w = inp.workload
     x, Wg, WuT, Wd = dev(inp)
@@ -111,14 +121,37 @@ def test_components_compose(name):
     p = tw.gate_pack(x, Wg, w.T, w.C)
     g = host_packing(p)
     assert np.array_equal(view["counts"], g["counts"]) and np.array_equal(view["ovf"], g["ovf"])
-    y = tw.fused_updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
+    updown = tw.sliced_updown if sliced_ok(w.d) else tw.fused_updown
+    y = updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
     yh = y.cpu().numpy()
     ovf = g["ovf"]
     fit = np.setdiff1d(np.arange(w.M), ovf)
-    assert np.isnan(yh[ovf]).all(), "fused kernel wrote an overflow row"
+    assert np.isnan(yh[ovf]).all(), "up/down kernel wrote an overflow row"
     assert np.isfinite(yh[fit]).all()
     tw.dense_fallback(x, Wg, WuT, Wd, p, y)
     assert np.array_equal(y.cpu().numpy().view(np.uint32), y_full.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_updown_kernels_match_definition(name):
+    """Both up/down forms, each completed by the fallback, against the fp64
+    definition, and against each other."""
+    inp, _, _, Y = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    p = tw.gate_pack(x, Wg, w.T, w.C)
+    g = host_packing(p)
+    outs = {}
+    forms = [("fused", tw.fused_updown)] + ([("sliced", tw.sliced_updown)] if sliced_ok(w.d) else [])
+    for label, fn in forms:
+        y = fn(x, WuT, Wd, p, y=nan_y(w.M, w.d))
+        tw.dense_fallback(x, Wg, WuT, Wd, p, y)
+        outs[label] = y.cpu().numpy()
+        rel, mx = check_y(outs[label], Y)
+        print(f"{name} [{label}]: rel L2 {rel:.2e}, max abs {mx:.2e}, overflow rows {g['n_ovf']}")
+    if "sliced" in outs:
+        a, b = outs["fused"], outs["sliced"]
+        assert np.abs(a - b).max() <= 1e-5 * max(np.abs(a).max(), 1e-30)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -232,3 +265,10 @@ def test_full_size(name):
     Ys = O.ffn_from_active_set(xs, inp.WuT, inp.Wd, Zs)
     rel, mx = check_y(yh[rows], Ys)
     print(f"[full] {name}: overflow rows {view['n_ovf']}, sampled rel L2 {rel:.2e}, max abs {mx:.2e}")
+
+    # the single-kernel up/down form on the same packing, on the same sampled rows
+    p = tw.gate_pack(x, Wg, w.T, w.C)
+    yf = tw.fused_updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
+    tw.dense_fallback(x, Wg, WuT, Wd, p, yf)
+    rel_f, _ = check_y(yf.cpu().numpy()[rows], Ys)
+    print(f"[full] {name}: fused form sampled rel L2 {rel_f:.2e}")
