@@ -43,7 +43,7 @@ _SIGNATURES = {
     "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
     "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "twell_sliced_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
-    "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "twell_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32]),
@@ -252,15 +252,17 @@ def sliced_updown(x, WuT, Wd, packed: Packed, y=None, workspace=None):
     return y
 
 
-def dense_fallback(x, Wg, WuT, Wd, packed: Packed, y, workspace=None):
+def dense_fallback(x, Wg, WuT, Wd, packed: Packed, y, workspace=None, ctrl=None):
     M, d = x.shape
     F = Wg.shape[0]
     args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
     y = _f32_out(y, "y", (M, d), x.device)
     ws = _workspace(workspace, x.device)
     wp, wn = ws.get(workspace_bytes(OP_DENSE_FALLBACK, M, d, F))
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
     pk = packed._c()
-    _check(lib().twell_dense_fallback(*args, ctypes.byref(pk), M, d, F, _dptr(y), wp, wn, _stream(x)),
+    _check(lib().twell_dense_fallback(*args, ctypes.byref(pk), M, d, F, _dptr(y), cp, cn, wp, wn, _stream(x)),
            "twell_dense_fallback")
     return y
 

@@ -12,8 +12,17 @@
 //
 // The fallback runs the same kernels over a device-side row list whose length
 // is only known on the device: both kernels are persistent (a fixed grid that
-// strides over the tiles the list needs), so no host synchronisation is needed
+// strides over the work the list needs), so no host synchronisation is needed
 // and an empty list costs one short launch each.
+//
+// A short list (a few overflow rows) gives few output tiles, each with a long
+// K loop (K = F = 8192 for the down product), which would leave most of the GPU
+// idle. Then the K loop of every tile is split S ways (S chosen on the device
+// from the list length): each split stores its fp32 partial tile in the
+// workspace, and the last split of a tile to finish (a per-tile arrival
+// counter in the control block, reset by that last split) adds the S partial
+// tiles in split order and runs the epilogue. The sum order is fixed, so the
+// result does not depend on which split finishes last.
 //
 // Workgroup tile 128 x 128, 4 waves as 2 x 2, each wave 64 x 64 (2 x 2 MFMA
 // 32x32x16 blocks), 32-wide K chunks double-buffered in LDS.
@@ -27,6 +36,113 @@ constexpr int kDM = 128, kDN = 128, kDK = 32;
 constexpr int kTile = kDM * kDK * 2;  // bytes of one 128 x 32 bf16 LDS tile
 constexpr int kPersistentWGs = 512;
 
+// Split-K policy of the gathering (fallback) kernels.
+constexpr int kSplitBelow = 128;   // split when there are fewer output tiles than this
+constexpr int kTargetItems = 256;  // aim for about this many (tile, split) work items
+constexpr int kMaxSplit = 16;
+constexpr int kMinSplitChunks = 8;  // K chunks of 32 per split at least
+
+struct SplitPlan {
+  int S, items;
+};
+
+__device__ __forceinline__ SplitPlan plan_split(bool allowed, int tiles, int nk) {
+  static_assert(kSplitBelow <= kDenseCounters / 2, "one arrival counter per split tile");
+  static_assert(2 * kTargetItems <= kDenseSplitSlots, "partial slots of the gated-up kernel");
+  if (!allowed || tiles == 0 || tiles >= kSplitBelow) return {1, tiles};
+  int S = kTargetItems / tiles;
+  S = min(S, min(kMaxSplit, max(nk / kMinSplitChunks, 1)));
+  S = max(S, 1);
+  return {S, tiles * S};
+}
+
+// Stores this thread's n fp32 accumulators (n / 4 float4) of split slot `slot`.
+template <int N>
+__device__ __forceinline__ void store_partial(float* part, int slot, const float (&v)[N]) {
+  float4* p = reinterpret_cast<float4*>(part) + static_cast<size_t>(slot) * (N / 4) * 256;
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q)
+    p[q * 256 + threadIdx.x] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+// v = sum over s = 0 .. S-1 of the partial accumulators stored in slots
+// slot0 + stride * s (this workgroup's own split included), in that order.
+// kPairs loads two slots per round (half the memory round trips, N / 2 more
+// registers).
+template <bool kPairs, int N>
+__device__ __forceinline__ void reduce_partials(const float* part, int slot0, int stride, int S, float (&v)[N]) {
+  const float4* base = reinterpret_cast<const float4*>(part);
+  auto slot_ptr = [&](int s) { return base + static_cast<size_t>(slot0 + stride * s) * (N / 4) * 256 + threadIdx.x; };
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = 0.f;
+  int s = 0;
+  for (; kPairs && s + 2 <= S; s += 2) {
+    const float4* p0 = slot_ptr(s);
+    const float4* p1 = slot_ptr(s + 1);
+    float4 t0[N / 4], t1[N / 4];
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      t0[q] = p0[q * 256];
+      t1[q] = p1[q * 256];
+    }
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      v[4 * q] = (v[4 * q] + t0[q].x) + t1[q].x;
+      v[4 * q + 1] = (v[4 * q + 1] + t0[q].y) + t1[q].y;
+      v[4 * q + 2] = (v[4 * q + 2] + t0[q].z) + t1[q].z;
+      v[4 * q + 3] = (v[4 * q + 3] + t0[q].w) + t1[q].w;
+    }
+  }
+  for (; s < S; ++s) {
+    const float4* p0 = slot_ptr(s);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 t = p0[q * 256];
+      v[4 * q] += t.x;
+      v[4 * q + 1] += t.y;
+      v[4 * q + 2] += t.z;
+      v[4 * q + 3] += t.w;
+    }
+  }
+}
+
+// Flattened views of a wave's 2 x 2 block of 32x32 accumulators.
+__device__ __forceinline__ void flatten(const f32x16_t (&acc)[2][2], float (&v)[64]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[(i * 2 + j) * 16 + k] = acc[i][j][k];
+}
+
+__device__ __forceinline__ void unflatten(const float (&v)[64], f32x16_t (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[i][j][k] = v[(i * 2 + j) * 16 + k];
+}
+
+// After a split has stored its partial tile: returns (to every thread of the
+// workgroup) whether it was the tile's last split to arrive. The last one
+// resets the tile's counter and may then read every split's partial tile.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int S, int* s_flag) {
+  __syncthreads();  // every wave's partial stores have completed
+  if (threadIdx.x == 0) {
+    __threadfence();  // ... and are visible to the other XCDs
+    const uint32_t old = atomicAdd(counter, 1u);
+    const bool last = old == static_cast<uint32_t>(S - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last) __threadfence();  // see the other splits' partial tiles
+  return last;
+}
+
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
@@ -37,9 +153,11 @@ __device__ __forceinline__ f32x16_t zero16() {
 template <bool kGather, bool kSplit>
 __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kTile];
+  __shared__ int s_last;
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
   const int tiles_m = (R + kDM - 1) / kDM;
-  const int ntiles = tiles_m * tiles_n;
+  const int nk = a.d / kDK;
+  const SplitPlan plan = plan_split(kGather && a.counters != nullptr, tiles_m * tiles_n, nk);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -48,7 +166,9 @@ __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles
   const uint32_t so[2] = {lds_off(lrow, lpc), lds_off(lrow + 64, lpc)};
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  for (int item = blockIdx.x; item < plan.items; item += gridDim.x) {
+    const int tile = item / plan.S, sp = item % plan.S;
+    const int kb = sp * nk / plan.S, ke = (sp + 1) * nk / plan.S;  // this split's K chunks
     const int m0 = (tile % tiles_m) * kDM;
     const int n0 = (tile / tiles_m) * kDN;
     const uint16_t *pa[2], *pg[2], *pu[2];
@@ -90,13 +210,12 @@ __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles
 #pragma unroll
       for (int j = 0; j < 2; ++j) ag[i][j] = au[i][j] = zero16();
 
-    const int nk = a.d / kDK;
-    gload(0);
+    gload(kb * kDK);
     sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kDK);
+    for (int kt = kb; kt < ke; ++kt) {
+      const int st = (kt - kb) & 1;
+      if (kt + 1 < ke) gload((kt + 1) * kDK);
       const uint8_t* As = smem + st * 3 * kTile;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -115,8 +234,23 @@ __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles
             au[i][j] = mfma_32x32x16(af[i], uf[j], au[i][j]);
           }
       }
-      if (kt + 1 < nk) sstore(st ^ 1);
+      if (kt + 1 < ke) sstore(st ^ 1);
       __syncthreads();
+    }
+
+    if (plan.S > 1) {  // slots 2 * item (z) and 2 * item + 1 (u) of 64 floats a thread
+      float v[64];
+      flatten(ag, v);
+      store_partial(a.part, 2 * item, v);
+      flatten(au, v);
+      store_partial(a.part, 2 * item + 1, v);
+      if (!arrive_last(&a.counters[a.counter_base + tile], plan.S, &s_last)) continue;
+      // slots of split s: 2 (tile S + s) and 2 (tile S + s) + 1
+      float z[64];
+      reduce_partials<false>(a.part, 2 * tile * plan.S, 2, plan.S, z);
+      unflatten(z, ag);
+      reduce_partials<false>(a.part, 2 * tile * plan.S + 1, 2, plan.S, z);
+      unflatten(z, au);
     }
 
 #pragma unroll
@@ -144,9 +278,11 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   constexpr int kNA = kSplit ? 2 : 1;
   constexpr int kStage = (kNA + 1) * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ int s_last;
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
   const int tiles_m = (R + kDM - 1) / kDM;
-  const int ntiles = tiles_m * tiles_n;
+  const int nk = a.F / kDK;
+  const SplitPlan plan = plan_split(kGather && a.counters != nullptr, tiles_m * tiles_n, nk);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -160,7 +296,9 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   for (int q = 0; q < 4; ++q) sbo[q] = lds_off(ng * 4 + q, kg >> 1) + (kg & 1) * 8;
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  for (int item = blockIdx.x; item < plan.items; item += gridDim.x) {
+    const int tile = item / plan.S, sp = item % plan.S;
+    const int kb = sp * nk / plan.S, ke = (sp + 1) * nk / plan.S;
     const int m0 = (tile % tiles_m) * kDM;
     const int n0 = (tile / tiles_m) * kDN;
     const uint16_t* pa[kNA][2];
@@ -212,13 +350,12 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-    const int nk = a.F / kDK;
-    gload(0);
+    gload(kb * kDK);
     sstore(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kDK);
+    for (int kt = kb; kt < ke; ++kt) {
+      const int st = (kt - kb) & 1;
+      if (kt + 1 < ke) gload((kt + 1) * kDK);
       const uint8_t* base = smem + st * kStage;
       const uint8_t* Bs = base + kNA * kTile;
 #pragma unroll
@@ -237,8 +374,17 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
         }
       }
-      if (kt + 1 < nk) sstore(st ^ 1);
+      if (kt + 1 < ke) sstore(st ^ 1);
       __syncthreads();
+    }
+
+    if (plan.S > 1) {
+      float v[64];
+      flatten(acc, v);
+      store_partial(a.part, item, v);
+      if (!arrive_last(&a.counters[a.counter_base + tile], plan.S, &s_last)) continue;
+      reduce_partials<true>(a.part, tile * plan.S, 1, plan.S, v);
+      unflatten(v, acc);
     }
 
 #pragma unroll
@@ -267,10 +413,13 @@ hipError_t launch_pair(const DenseArgs& a, hipStream_t s) {
     g1 = g1 < kPersistentWGs ? g1 : kPersistentWGs;
     g2 = g2 < kPersistentWGs ? g2 : kPersistentWGs;
   }
-  gated_up_kernel<kGather, kSplit><<<dim3(g1), dim3(256), 0, s>>>(a, tiles_nf);
+  DenseArgs up = a, down = a;
+  up.counter_base = 0;
+  down.counter_base = kDenseCounters / 2;
+  gated_up_kernel<kGather, kSplit><<<dim3(g1), dim3(256), 0, s>>>(up, tiles_nf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  down_kernel<kGather, kSplit><<<dim3(g2), dim3(256), 0, s>>>(a, tiles_nd);
+  down_kernel<kGather, kSplit><<<dim3(g2), dim3(256), 0, s>>>(down, tiles_nd);
   return hipGetLastError();
 }
 

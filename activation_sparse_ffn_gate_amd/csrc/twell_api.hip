@@ -16,10 +16,16 @@ constexpr int64_t kMaxF = int64_t(1) << 24;
 
 struct Layout {
   size_t vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0, part = 0;
+  size_t split = 0;  // the split-K fallback's partial tiles
   size_t total = 0;
 };
 
-size_t ctrl_bytes(int64_t M) { return twell::kCtrlBytes + align256(size_t(M) * 4); }
+// Header, one flag per row, then the fallback's arrival counters.
+size_t ctrl_flags_bytes(int64_t M) { return twell::kCtrlBytes + align256(size_t(M) * 4); }
+size_t ctrl_bytes(int64_t M) { return ctrl_flags_bytes(M) + align256(twell::kDenseCounters * 4); }
+uint32_t* fallback_counters(void* ctrl, int64_t M) {
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ctrl) + ctrl_flags_bytes(M));
+}
 
 // Offsets inside the workspace of each operation (all 256-byte aligned).
 Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
@@ -41,13 +47,16 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
       L.counts = take(m * nT * 2);
       L.ovf_rows = take(m * 4);
       L.n_ovf = take(4);
-      // The up/down partials and the fallback's hidden pair are live at
-      // different times of the stream, so they share one region.
+      // The up/down kernels' buffers and the fallback's (hidden pair and
+      // partial tiles) are live at different times of the stream, so they
+      // share one region.
       const size_t h_bytes = align256(m * f * 2);
-      const size_t scratch = take(std::max(2 * h_bytes, twell::sliced_layout(M, F, T, C).total));
+      const size_t fb_bytes = 2 * h_bytes + twell::kDenseSplitBytes;
+      const size_t scratch = take(std::max(fb_bytes, twell::sliced_layout(M, F, T, C).total));
       L.part = scratch;
       L.h_hi = scratch;
       L.h_lo = scratch + h_bytes;
+      L.split = scratch + 2 * h_bytes;
       break;
     }
     case TWELL_OP_SLICED_UPDOWN:
@@ -59,6 +68,7 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
     case TWELL_OP_DENSE_FALLBACK:
       L.h_hi = take(m * f * 2);
       L.h_lo = take(m * f * 2);
+      L.split = take(twell::kDenseSplitBytes);
       break;
     default:
       return L;
@@ -185,7 +195,8 @@ int sliced_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, cons
 
 int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
                int64_t M, int64_t d, int64_t F, const int32_t* rows, const int32_t* n_rows,
-               uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s) {
+               uint16_t* h_hi, uint16_t* h_lo, float* y, float* split_part, uint32_t* counters,
+               hipStream_t s) {
   if (M == 0) return TWELL_OK;
   twell::DenseArgs a;
   a.x = x;
@@ -200,6 +211,9 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   a.h_hi = h_hi;
   a.h_lo = h_lo;
   a.y = y;
+  a.part = split_part;
+  a.counters = counters;
+  a.counter_base = 0;
   return hip_status(twell::launch_dense(a, s));
 }
 
@@ -247,16 +261,19 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
 
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                          const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
-                         int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream) {
+                         int64_t F, float* y, void* ctrl, size_t ctrl_bytes_, void* workspace,
+                         size_t ws_bytes, void* stream) {
   if (!Wg || !WuT || !Wd || !in || !in->n_ovf) return TWELL_E_INVALID_ARG;
   if (M != 0 && (!x || !y || !in->ovf_rows)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, in->ovf_rows, in->n_ovf, at<uint16_t>(workspace, L.h_hi),
-                    at<uint16_t>(workspace, L.h_lo), y, static_cast<hipStream_t>(stream));
+                    at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
+                    fallback_counters(ctrl, M), static_cast<hipStream_t>(stream));
 }
 
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
@@ -281,7 +298,8 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
   if (st != TWELL_OK) return st;
   return dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
-                    at<uint16_t>(workspace, L.h_lo), y, s);
+                    at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
+                    fallback_counters(ctrl, M), s);
 }
 
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
@@ -294,7 +312,7 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
   if (st != TWELL_OK) return st;
   const Layout L = layout(TWELL_OP_DENSE_FFN, M, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, nullptr, nullptr, at<uint16_t>(workspace, L.h_hi),
-                    nullptr, y, static_cast<hipStream_t>(stream));
+                    nullptr, y, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
 size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {

@@ -7,9 +7,9 @@
 
 namespace twell {
 
-// Control block of the gate kernel's overflow set, kept in the workspace:
-// ctrl[0] = entries appended this call, ctrl[1] = workgroups finished,
-// followed by one dedup flag per row. Zero between calls.
+// Control block of the gate kernel's overflow set: ctrl[0] = entries appended
+// this call, ctrl[1] = workgroups finished, then one dedup flag per row, then
+// kDenseCounters arrival counters of the split-K fallback. Zero between calls.
 constexpr size_t kCtrlBytes = 256;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -50,7 +50,17 @@ struct DenseArgs {
   uint16_t* h_hi;         // [M, F] bf16 hidden (or its high part)
   uint16_t* h_lo;         // [M, F] low part; nullptr: plain bf16 hidden
   float* y;
+  // Split-K of the gathering kernels (nullptr counters: no split).
+  float* part;            // kDenseSplitSlots partial tiles of 64 KB
+  uint32_t* counters;     // zeroed; gated-up tiles at [0, 128), down tiles at [128, 256)
+  int counter_base;       // set by the launcher for the down kernel
 };
+
+// Partial-tile slots of the split-K fallback: 2 per work item of the gated-up
+// kernel (z and u), 1 per item of the down kernel; at most 256 items.
+constexpr int kDenseSplitSlots = 512;
+constexpr size_t kDenseSplitBytes = size_t(kDenseSplitSlots) * 64 * 1024;
+constexpr int kDenseCounters = 256;
 
 // Up + down projections split into kSlices column slices of d, one per XCD.
 constexpr int kSlices = 8;

@@ -30,13 +30,14 @@
  *    twell_workspace_bytes(op, ...) bytes, 256-byte aligned, contents
  *    irrelevant. One workspace must not be used by two calls that may run
  *    concurrently.
- *  - Control block (twell_gate_pack, twell_ffn_forward): a caller-owned device
- *    buffer of at least twell_ctrl_bytes(M) bytes, 256-byte aligned, used only
- *    for this purpose. It must be zero-filled before its first use; every call
- *    leaves it zero-filled again when it completes (stream order), so one
- *    buffer sized for the largest M serves every later call. It holds the
- *    overflow-set counters and one deduplication flag per row. Calls sharing a
- *    control block must not run concurrently.
+ *  - Control block (twell_gate_pack, twell_dense_fallback, twell_ffn_forward):
+ *    a caller-owned device buffer of at least twell_ctrl_bytes(M) bytes,
+ *    256-byte aligned, used only for this purpose. It must be zero-filled
+ *    before its first use; every call leaves it zero-filled again when it
+ *    completes (stream order), so one buffer sized for the largest M serves
+ *    every later call. It holds the overflow-set counters, one deduplication
+ *    flag per row and the arrival counters of the fallback's split products.
+ *    Calls sharing a control block must not run concurrently.
  *  - With M == 0 nothing is computed; x and y may then be NULL.
  */
 #ifndef TWELL_H_
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 1
+#define TWELL_ABI_VERSION 2
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -129,11 +130,14 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
  * in in->ovf_rows it computes y[r] = (ReLU(x_r Wg^T) ⊙ x_r WuT^T) Wd with bf16
  * MFMA products, fp32 accumulation and the hidden vector carried as a bf16
  * hi/lo pair. n_ovf is read on the device (no host synchronisation); other rows
- * of y are untouched.
+ * of y are untouched. When the list is short the K loops are split over more
+ * workgroups and their partial tiles added in a fixed order (deterministic).
+ * ctrl: >= twell_ctrl_bytes(M) (see above);
  * workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FALLBACK, ...). */
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                          const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d,
-                         int64_t F, float* y, void* workspace, size_t ws_bytes, void* stream);
+                         int64_t F, float* y, void* ctrl, size_t ctrl_bytes, void* workspace,
+                         size_t ws_bytes, void* stream);
 
 /* The whole sparse forward: twell_gate_pack, then twell_sliced_updown (or
  * twell_fused_updown for the d that the sliced form does not support), then

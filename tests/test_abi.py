@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 1
+    assert L.twell_abi_version() == 2
     for s in (OK, E_ARG, E_UNSUP, E_WS, -4):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"
@@ -37,14 +37,14 @@ def test_workspace_sizes(M, d, F, T, C):
     f = tw.workspace_bytes(tw.OP_FFN_FORWARD, M, d, F, T, C)
     dn = tw.workspace_bytes(tw.OP_DENSE_FFN, M, d, F)
     fb = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, M, d, F)
-    assert g >= 256 + 4 * M and g % 256 == 0
+    assert g >= 256 + 4 * M + 4 * 256 and g % 256 == 0  # header, row flags, split counters
     assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + 4 * M * F
-    assert dn >= 2 * M * F and fb >= 4 * M * F
+    assert dn >= 2 * M * F and fb >= 4 * M * F + 512 * 65536  # hidden pair + split partial tiles
     assert f % 256 == 0 and dn % 256 == 0
     sl = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, M, d, F, T, C)
     assert sl >= 8 * M * nT * C * 4 and sl % 256 == 0
     # the forward's scratch holds either the sliced partials or the fallback's hidden pair
-    assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + max(sl - 256, 4 * M * F)
+    assert f >= M * nT * C * 5 + M * nT * 2 + 4 * M + max(sl - 256, 4 * M * F + 512 * 65536)
 
 
 @pytest.mark.parametrize("d,ok", [(256, True), (768, True), (2048, True), (2560, True), (4096, True),
@@ -126,8 +126,10 @@ def test_forward_validation():
     assert sl(FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, 64, 8, FAKE, None, sws, None) == E_WS
     fb = L.twell_dense_fallback
     fws = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, 256, 256, 1024)
-    assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, FAKE, fws - 1, None) == E_WS
-    assert fb(FAKE, FAKE, FAKE, FAKE, None, 256, 256, 1024, FAKE, FAKE, fws, None) == E_ARG
+    assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, FAKE, cb, FAKE, fws - 1, None) == E_WS
+    assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, None, cb, FAKE, fws, None) == E_WS
+    assert fb(FAKE, FAKE, FAKE, FAKE, ctypes.byref(pk), 256, 256, 1024, FAKE, FAKE, cb - 1, FAKE, fws, None) == E_WS
+    assert fb(FAKE, FAKE, FAKE, FAKE, None, 256, 256, 1024, FAKE, FAKE, cb, FAKE, fws, None) == E_ARG
 
 
 def test_packed_view_is_host_arithmetic():
