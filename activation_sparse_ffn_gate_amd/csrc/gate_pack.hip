@@ -307,20 +307,21 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
     }
   }
 
-  // The last workgroup publishes n_ovf and clears the control block. Only a
-  // workgroup that appended rows has list entries to release to it. The
-  // stage buffers are idle now and hold the workgroup's flags.
-  int* sflag = reinterpret_cast<int*>(smem);  // [0] = last, [1 + w] = wave appended
-  const int wave_appended = __ballot(appended) != 0 ? 1 : 0;
-  __syncthreads();
-  if (lane == 0) sflag[1 + w] = wave_appended;
-  __syncthreads();
+  // The last workgroup publishes n_ovf and clears the control block. Only the
+  // waves that appended rows have list entries to release to it: each of them
+  // releases its own (the fence waits for that wave's stores); the other waves
+  // go on without waiting for their packing stores to drain, so the barriers
+  // below carry no memory fence. The stage buffers are idle now and hold the
+  // workgroup's flag.
+  int* sflag = reinterpret_cast<int*>(smem);  // [0] = this workgroup finished last
+  if (__ballot(appended) != 0) __threadfence();
+  raw_barrier();  // every wave is past its appends (and their release) and done with LDS
   if (tid == 0) {
-    if (sflag[1] | sflag[2] | sflag[3] | sflag[4]) __threadfence();
     const uint32_t done = atomicAdd(&a.ctrl[1], 1u);
     sflag[0] = (done == static_cast<uint32_t>(gridDim.x) - 1u);
   }
-  __syncthreads();
+  waitcnt<63, 0>();  // the flag store has reached LDS
+  raw_barrier();
   if (sflag[0]) {
     __threadfence();
     uint32_t n = __hip_atomic_load(&a.ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
