@@ -1,13 +1,18 @@
 """Throughput of the TwELL sparse gated-FFN forward on one MI355X.
 
-One step = one twell_ffn_forward (gate GEMM + TwELL packing, fused up+down
-over the packed non-zeros, dense fallback of overflow rows) over the whole
-synthetic layer, inputs resident in HBM. Prints ONE JSON line.
+One step = one twell_ffn_forward (gate GEMM + TwELL packing, up+down
+projections over the packed non-zeros, dense fallback of overflow rows) over
+the whole synthetic layer, inputs resident in HBM. Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-sweep]
 
 The default workload is the 1.5B-like layer: M=4096 tokens, d=2048, F=8192,
-about 29 active gate units per token, T=128, C=16.
+about 29 active gate units per token, T=128, C=16. Besides the headline the
+line carries per-kernel times, the roofline of the dominant kernel, warm and
+cold (MALL flushed) latency percentiles of one forward, the dense baselines
+(this library's MFMA kernels and a hipBLASLt one through torch) and a
+density sweep (M=8192, d=2048, F=8192 at 0.1 .. 11 % active units) with the
+sparse/dense ratio at every point.
 """
 
 from __future__ import annotations
@@ -41,8 +46,9 @@ def sources_hash():
     return h.hexdigest()
 
 
-def _counter_kib(path, counter):
-    """Mean per-dispatch value of one rocprofv3 --pmc counter (KiB)."""
+def _counter_kib(path, counter, kernel=None):
+    """Mean per-dispatch value of one rocprofv3 --pmc counter (KiB), over the
+    dispatches whose kernel name contains `kernel` (all if None)."""
     import csv
     import glob
 
@@ -50,7 +56,7 @@ def _counter_kib(path, counter):
     for fn in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
         with open(fn) as f:
             for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
+                if r["Counter_Name"] == counter and (kernel is None or kernel in r["Kernel_Name"]):
                     vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not vals:
         raise SystemExit(f"no {counter} readings under {path}")
@@ -59,17 +65,21 @@ def _counter_kib(path, counter):
 
 def record_traffic(root, workload):
     """Write profiles/traffic.json from rocprofv3 --pmc runs stored under root:
-    pmc_<leg>_fetch / pmc_<leg>_write for leg in gate, fused and copy."""
+    pmc_<leg>_fetch / pmc_<leg>_write for leg in gate, fused, sliced and copy
+    (the sliced leg holds both of its kernels; their traffic is summed)."""
     cf = COPY_BYTES / 1024.0 / _counter_kib(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE")
     cw = COPY_BYTES / 1024.0 / _counter_kib(os.path.join(root, "pmc_copy_write"), "WRITE_SIZE")
     rec = {"sources_sha256": sources_hash(), "calibration": {"fetch_factor": cf, "write_factor": cw,
                                                              "copy_bytes": COPY_BYTES}, "workloads": {}}
     ent = {}
-    for leg, kernel in (("gate", "gate_pack"), ("fused", "fused_updown")):
-        fk = _counter_kib(os.path.join(root, f"pmc_{leg}_fetch"), "FETCH_SIZE")
-        wk = _counter_kib(os.path.join(root, f"pmc_{leg}_write"), "WRITE_SIZE")
-        ent[kernel] = {"fetch_kib_raw": fk, "write_kib_raw": wk,
-                       "traffic_bytes": fk * 1024.0 * cf + wk * 1024.0 * cw}
+    for leg, name, kernels in (("gate", "gate_pack", ["gate_pack"]), ("fused", "fused_updown", ["fused_updown"]),
+                               ("sliced", "sliced_updown", ["sliced_up_kernel", "sliced_down_kernel"])):
+        if not os.path.isdir(os.path.join(root, f"pmc_{leg}_fetch")):
+            continue
+        fk = sum(_counter_kib(os.path.join(root, f"pmc_{leg}_fetch"), "FETCH_SIZE", k) for k in kernels)
+        wk = sum(_counter_kib(os.path.join(root, f"pmc_{leg}_write"), "WRITE_SIZE", k) for k in kernels)
+        ent[name] = {"fetch_kib_raw": fk, "write_kib_raw": wk,
+                     "traffic_bytes": fk * 1024.0 * cf + wk * 1024.0 * cw}
     rec["workloads"][workload] = ent
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
@@ -90,6 +100,8 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc outputs under DIR (no GPU needed)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the density sweep")
+    ap.add_argument("--sweep-steps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -104,6 +116,89 @@ def time_loop(fn, steps, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / steps  # ms per call
+
+
+def latency(fn, n, flush=None):
+    """Median / p10 / p90 milliseconds of single calls, each timed with HIP
+    events on the current stream. With `flush` (a 512 MB buffer) the caches,
+    MALL included, are overwritten before every call (outside the events)."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush.fill_(1)  # also keeps the GPU busy while the timed call is queued
+        else:
+            fn()  # an untimed call in front keeps the timed one from waiting on the host
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        e.synchronize()
+        ts.append(s.elapsed_time(e))
+    q = np.percentile(ts, [50, 10, 90])
+    return {"median_ms": round(float(q[0]), 5), "p10_ms": round(float(q[1]), 5), "p90_ms": round(float(q[2]), 5),
+            "n": n}
+
+
+def dense_torch(x, Wg, WuT, Wd):
+    """The dense gated FFN on hipBLASLt through torch (bf16 products, bf16
+    hidden): z|u = x [Wg; WuT]^T in one GEMM, h = ReLU(z) * u, y = h Wd."""
+    import torch
+
+    F = Wg.shape[0]
+    Wgu = torch.cat([Wg, WuT], 0).contiguous()
+
+    def run():
+        zu = torch.nn.functional.linear(x, Wgu)
+        h = torch.relu(zu[:, :F]) * zu[:, F:]
+        return h @ Wd
+
+    return run
+
+
+def density_sweep(dev, steps, warmup):
+    """Sparse forward vs the dense baselines at every sweep density."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+    from synth import WORKLOADS, make_inputs
+
+    out = []
+    for name in sorted((k for k in WORKLOADS if k.startswith("sweep_")), key=lambda k: WORKLOADS[k].mean_nnz):
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        x, Wg, WuT, Wd = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+                          for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+        y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
+        ws, ctrl, wsd = tw.Workspace(dev), tw.Workspace(dev, zeroed=True), tw.Workspace(dev)
+        stream = torch.cuda.current_stream(dev)
+        fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)  # noqa: E731
+        dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y, workspace=wsd)  # noqa: E731
+        dt = dense_torch(x, Wg, WuT, Wd)
+        res = {}
+        for key, fn in (("sparse", fwd), ("dense", dense), ("dense_hipblaslt", dt)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            res[key] = time_loop(fn, steps, stream)
+        view = tw.packed_view(w.M, w.d, w.F, w.T, w.C, workspace=ws, device=dev)
+        counts = view.counts.cpu().numpy().view(np.uint16).astype(np.int64)
+        out.append({
+            "workload": name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C,
+            "active_pct": round(100.0 * counts.sum() / (w.M * w.F), 3),
+            "overflow_rows": int(view.n_ovf.item()),
+            "sparse_ms": round(res["sparse"], 5), "dense_ms": round(res["dense"], 5),
+            "dense_hipblaslt_ms": round(res["dense_hipblaslt"], 5),
+            "speedup_vs_dense": round(res["dense"] / res["sparse"], 3),
+            "speedup_vs_dense_hipblaslt": round(res["dense_hipblaslt"] / res["sparse"], 3),
+        })
+        del x, Wg, WuT, Wd, y, ws, ctrl, wsd, dt, view
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(inp, budget_s):
@@ -218,7 +313,8 @@ def main():
     nnz_fit = int(counts[fit].sum())
     nnz_all = int(counts.sum())
     k_steps = max(args.steps, 20)
-    legs = [gate, fused, fallback, dense] + ([sliced] if sliced_ok else [])
+    dense_tl = dense_torch(x, Wg, WuT, Wd)
+    legs = [gate, fused, fallback, dense, dense_tl] + ([sliced] if sliced_ok else [])
     for fn in legs:
         fn()
     torch.cuda.synchronize()
@@ -227,6 +323,10 @@ def main():
     t_sliced = time_loop(sliced, k_steps, stream) if sliced_ok else None
     t_fb = time_loop(fallback, k_steps, stream)
     t_dense = time_loop(dense, k_steps, stream)
+    t_dense_tl = time_loop(dense_tl, k_steps, stream)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    lat = {"warm": latency(fwd, 20), "cold": latency(fwd, 20, flush=flush)}
+    del flush
     # the up/down form twell_ffn_forward runs
     t_updown = t_sliced if sliced_ok else t_fused
     updown_name = "sliced_updown" if sliced_ok else "fused_updown"
@@ -285,13 +385,19 @@ def main():
             "nnz_per_token": round(nnz_all / w.M, 3),
             "overflow_rows": n_ovf,
         },
+        "latency_forward": lat,
         "dense_baseline": {
             "ms": round(t_dense, 5),
             "tokens_per_s": round(w.M / (t_dense * 1e-3), 1),
             "tflops": round(3 * gate_flops / (t_dense * 1e-3) / 1e12, 1),
             "speedup_sparse_vs_dense": round(t_dense / ms_step, 3),
+            "hipblaslt_ms": round(t_dense_tl, 5),
+            "hipblaslt_tflops": round(3 * gate_flops / (t_dense_tl * 1e-3) / 1e12, 1),
+            "speedup_sparse_vs_hipblaslt": round(t_dense_tl / ms_step, 3),
         },
     }
+    if not args.no_sweep:  # HBM holds both layers' buffers easily
+        out["density_sweep"] = density_sweep(dev, args.sweep_steps, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))
