@@ -44,7 +44,15 @@ namespace {
 
 constexpr int kRowsPerWG = 4;      // one wave per (row, slice)
 constexpr int kListCap = 256;       // stored units staged per wave per round
+constexpr int kListPad = 64;        // staged lists are padded (unit 0, value 0) to a whole step
 constexpr int kCountGroups = 2;     // rows of up to 128 tiles keep their counts in registers
+
+// 16 bytes at a 32-bit byte offset from a wave-uniform base (the weight
+// matrices are below 2 GiB, checked by the host), so the address needs no
+// 64-bit vector arithmetic.
+__device__ __forceinline__ u32x4_t ldg16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + off);
+}
 
 // Sum over aligned groups of L lanes; every lane of a group gets the sum.
 template <int L>
@@ -128,8 +136,8 @@ __device__ __forceinline__ int stage_row(const SlicedArgs& a, int row, const int
 template <int L, int V, int U>
 __global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
-  __shared__ int s_j[kRowsPerWG][kListCap];
-  __shared__ float s_g[kRowsPerWG][kListCap];
+  __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
+  __shared__ float s_g[kRowsPerWG][kListCap + kListPad];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -166,17 +174,24 @@ __global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
   int* lj = s_j[w];
   float* lg = s_g[w];
 
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const uint32_t col_bytes = static_cast<uint32_t>(col0) * 2u;
   const int total = stage_row<true>(a, row, c, lj, lg, [&](int n, int e0) {
     if (slice == 0)  // the row's unit list, for the down pass
       for (int i = lane; i < n; i += 64) urow[e0 + i] = lj[i];
+    static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the list");
+    if (lane < kListPad) {  // pad to a whole step: unit 0 (a valid row), value 0
+      lj[n + lane] = 0;
+      lg[n + lane] = 0.f;
+    }
+    wave_lds_sync();
     for (int e = 0; e < n; e += G * U) {
       u32x4_t wu[U][V];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = lj[min(e + u * G + grp, n - 1)];
-        const uint16_t* p = a.WuT + static_cast<size_t>(j) * a.d + col0;
+        const uint32_t off = static_cast<uint32_t>(lj[e + u * G + grp]) * row_bytes + col_bytes;
 #pragma unroll
-        for (int v = 0; v < V; ++v) wu[u][v] = gload16(p + v * 8 * L);
+        for (int v = 0; v < V; ++v) wu[u][v] = ldg16(a.WuT, off + v * 16 * L);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -199,8 +214,8 @@ __global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
 template <int L, int V, int U>
 __global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
-  __shared__ int s_j[kRowsPerWG][kListCap];
-  __shared__ float s_h[kRowsPerWG][kListCap];
+  __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
+  __shared__ float s_h[kRowsPerWG][kListCap + kListPad];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -216,6 +231,8 @@ __global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
   const size_t cap = static_cast<size_t>(a.F / a.T) * a.C;
   const size_t slice_stride = static_cast<size_t>(a.M) * cap;
   const float* prow = a.part + static_cast<size_t>(row) * cap;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const uint32_t col_bytes = static_cast<uint32_t>(col0) * 2u;
   const int32_t* urow = a.units + static_cast<size_t>(row) * cap;
   int* lj = s_j[w];
   float* lh = s_h[w];
@@ -237,6 +254,11 @@ __global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
       for (int s = 0; s < kSlices; ++s) h += prow[s * slice_stride + e0 + i];
       lh[i] = h;
     }
+    static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the list");
+    if (lane < kListPad) {  // pad to a whole step: unit 0 (a valid row), h 0
+      lj[m + lane] = 0;
+      lh[m + lane] = 0.f;
+    }
     wave_lds_sync();
     for (int e = 0; e < m; e += G * U) {
       u32x4_t wd[U][V];
@@ -244,11 +266,10 @@ __global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = e + u * G + grp;
-        const int j = lj[min(k, m - 1)];
-        hv[u] = (k < m) ? lh[k] : 0.f;
-        const uint16_t* p = a.Wd + static_cast<size_t>(j) * a.d + col0;
+        hv[u] = lh[k];
+        const uint32_t off = static_cast<uint32_t>(lj[k]) * row_bytes + col_bytes;
 #pragma unroll
-        for (int v = 0; v < V; ++v) wd[u][v] = gload16(p + v * 8 * L);
+        for (int v = 0; v < V; ++v) wd[u][v] = ldg16(a.Wd, off + v * 16 * L);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -289,32 +310,50 @@ __global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
   }
 }
 
-// Loads in flight per lane per step: about 4 sixteen-byte vectors (deeper
-// unrolling costs more in occupancy than it gains).
+// Loads in flight per lane per step. Up pass: about 8 sixteen-byte vectors.
+// Down pass: about 4 (deeper unrolling costs more in occupancy than it gains).
+template <int L, int V>
+constexpr int unroll_up() {  // also at most L, so a step spans at most 64 entries
+  return (V >= 8 ? 1 : 8 / V) < L ? (V >= 8 ? 1 : 8 / V) : L;
+}
 template <int V>
-constexpr int unroll_for() {
+constexpr int unroll_down() {
   return V <= 1 ? 4 : (V <= 2 ? 2 : 1);
 }
 
 template <int L, int V>
 hipError_t launch_up(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
-  sliced_up_kernel<L, V, unroll_for<V>()><<<grid, block, 0, s>>>(a);
+  sliced_up_kernel<L, V, unroll_up<L, V>()><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int L, int V>
 hipError_t launch_down(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
-  sliced_down_kernel<L, V, unroll_for<V>()><<<grid, block, 0, s>>>(a);
+  sliced_down_kernel<L, V, unroll_down<V>()><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
-// pieces = d / 64 sixteen-byte pieces per slice row. Up pass: L = the largest
-// power of two <= 64 dividing pieces, V = pieces / L. Down pass: the same,
-// except that 32 < pieces < 64 uses one group of `pieces` lanes (V = 1).
-bool lane_split(int d, bool down, int* L, int* V) {
+// A slice row is pieces = d / 64 sixteen-byte pieces, read by groups of L
+// lanes holding V = pieces / L pieces each.
+// Up pass: narrow groups (L = 8 where it divides, else 4; doubled while V > 8),
+// since every stored unit's partial product is summed within its group.
+// Down pass: wide groups (L = the largest power of two <= 64 dividing pieces,
+// V <= 7, or one group of `pieces` lanes when 32 < pieces < 64), since its
+// cross-group sum happens once per row.
+bool lane_split_up(int d, int* L, int* V) {
   if (d < 256 || d > 8192 || d % 256 != 0) return false;
   const int pieces = d / 64;
-  if (down && pieces > 32 && pieces < 64) {
+  int l = (pieces % 8 == 0) ? 8 : 4;
+  while (pieces / l > 8 && l < 64 && pieces % (2 * l) == 0) l *= 2;
+  *L = l;
+  *V = pieces / l;
+  return *V <= 8;
+}
+
+bool lane_split_down(int d, int* L, int* V) {
+  if (d < 256 || d > 8192 || d % 256 != 0) return false;
+  const int pieces = d / 64;
+  if (pieces > 32 && pieces < 64) {
     *L = pieces;
     *V = 1;
     return true;
@@ -326,17 +365,20 @@ bool lane_split(int d, bool down, int* L, int* V) {
   return *V <= 7;
 }
 
-// Instantiated (L, V) pairs; the switch key is L * 8 + V.
-#define TWELL_SLICED_SHAPES(X)                                                                   \
-  X(64, 1) X(64, 2) X(32, 1) X(32, 3) X(16, 1) X(16, 3) X(16, 5) X(16, 7) X(8, 1) X(8, 3) X(8, 5) \
-      X(8, 7) X(4, 1) X(4, 3) X(4, 5) X(4, 7)
-#define TWELL_WIDE_DOWN_SHAPES(X) X(40, 1) X(48, 1) X(56, 1)
+// Instantiated (L, V) pairs, one per supported d; the switch key is L * 16 + V.
+#define TWELL_UP_SHAPES(X)                                                                          \
+  X(4, 1) X(8, 1) X(4, 3) X(8, 2) X(4, 5) X(8, 3) X(4, 7) X(8, 4) X(8, 5) X(8, 6) X(8, 7) X(8, 8) \
+      X(16, 5) X(16, 6) X(16, 7) X(16, 8)
+#define TWELL_DOWN_SHAPES(X)                                                                      \
+  X(4, 1) X(8, 1) X(4, 3) X(16, 1) X(4, 5) X(8, 3) X(4, 7) X(32, 1) X(40, 1) X(48, 1) X(56, 1) \
+      X(64, 1) X(16, 5) X(32, 3) X(16, 7) X(64, 2)
 
 }  // namespace
 
-bool sliced_supports_d(int d) {
+bool sliced_supports(int64_t d, int64_t F) {
   int L, V;
-  return lane_split(d, false, &L, &V) && lane_split(d, true, &L, &V);
+  if (!lane_split_up(int(d), &L, &V) || !lane_split_down(int(d), &L, &V)) return false;
+  return F * d * 2 < (int64_t(1) << 31);  // 32-bit byte offsets into WuT and Wd
 }
 
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C) {
@@ -351,22 +393,24 @@ SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C) {
 
 hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s) {
   int Lu, Vu, Ld, Vd;
-  if (!lane_split(a.d, false, &Lu, &Vu) || !lane_split(a.d, true, &Ld, &Vd)) return hipErrorInvalidValue;
+  if (!sliced_supports(a.d, a.F)) return hipErrorInvalidValue;
+  lane_split_up(a.d, &Lu, &Vu);
+  lane_split_down(a.d, &Ld, &Vd);
   const dim3 grid(((a.M + kRowsPerWG - 1) / kRowsPerWG) * kSlices), block(64 * kRowsPerWG);
   hipError_t e = hipErrorInvalidValue;
-  switch (Lu * 8 + Vu) {
+  switch (Lu * 16 + Vu) {
 #define TWELL_CASE(L, V) \
-  case L * 8 + V: e = launch_up<L, V>(a, s, grid, block); break;
-    TWELL_SLICED_SHAPES(TWELL_CASE)
+  case L * 16 + V: e = launch_up<L, V>(a, s, grid, block); break;
+    TWELL_UP_SHAPES(TWELL_CASE)
 #undef TWELL_CASE
     default: break;
   }
   if (e != hipSuccess) return e;
   e = hipErrorInvalidValue;
-  switch (Ld * 8 + Vd) {
+  switch (Ld * 16 + Vd) {
 #define TWELL_CASE(L, V) \
-  case L * 8 + V: e = launch_down<L, V>(a, s, grid, block); break;
-    TWELL_SLICED_SHAPES(TWELL_CASE) TWELL_WIDE_DOWN_SHAPES(TWELL_CASE)
+  case L * 16 + V: e = launch_down<L, V>(a, s, grid, block); break;
+    TWELL_DOWN_SHAPES(TWELL_CASE)
 #undef TWELL_CASE
     default: break;
   }

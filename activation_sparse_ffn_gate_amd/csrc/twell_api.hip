@@ -251,7 +251,7 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
   if (M != 0 && (!x || !y || !in->vals || !in->idx || !in->counts)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
-  if (st == TWELL_OK && !twell::sliced_supports_d(int(d))) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK && !twell::sliced_supports(d, F)) st = TWELL_E_UNSUPPORTED;
   if (st == TWELL_OK) st = check_ws(TWELL_OP_SLICED_UPDOWN, M, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   const Layout L = layout(TWELL_OP_SLICED_UPDOWN, M, F, T, C);
@@ -292,7 +292,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   const twell_packed p = packed_in_ws(workspace, L);
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
-  if (twell::sliced_supports_d(int(d)))
+  if (twell::sliced_supports(d, F))
     st = sliced_impl(x, WuT, Wd, &p, M, d, F, T, C, at<uint8_t>(workspace, L.part), y, s);
   else
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
@@ -319,7 +319,7 @@ size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_
   if (check_dims(M, d, F) != TWELL_OK) return 0;
   if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD || op == TWELL_OP_SLICED_UPDOWN) {
     if (check_tc(F, T, C) != TWELL_OK) return 0;
-    if (op == TWELL_OP_SLICED_UPDOWN && !twell::sliced_supports_d(int(d))) return 0;
+    if (op == TWELL_OP_SLICED_UPDOWN && !twell::sliced_supports(d, F)) return 0;
   } else if (op == TWELL_OP_DENSE_FFN || op == TWELL_OP_DENSE_FALLBACK) {
     if (F % 64 != 0) return 0;
     T = 0;

@@ -86,7 +86,8 @@ struct SlicedLayout {
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
 hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
-bool sliced_supports_d(int d);
+// d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
+bool sliced_supports(int64_t d, int64_t F);
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
 hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);

@@ -118,8 +118,9 @@ int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* W
  * workspace: >= twell_workspace_bytes(TWELL_OP_SLICED_UPDOWN, ...)
  * = 8 * M * (F / T) * C fp32 partials.
  * d must be one of 256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072,
- * 3584, 4096, 5120, 6144, 7168, 8192 (d / 64 = 2^a * b with b in {1, 3, 5, 7}),
- * otherwise TWELL_E_UNSUPPORTED. */
+ * 3584, 4096, 5120, 6144, 7168, 8192 (d / 64 = 2^a * b with b in {1, 3, 5, 7})
+ * and F * d * 2 < 2^31 (each weight matrix below 2 GiB), otherwise
+ * TWELL_E_UNSUPPORTED. */
 int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd,
                         const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
                         int32_t C, float* y, void* workspace, size_t ws_bytes, void* stream);
