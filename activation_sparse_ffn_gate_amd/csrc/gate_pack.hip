@@ -9,9 +9,10 @@
 // MI355X mapping. One workgroup (4 waves, one per SIMD) computes a 256-token x
 // 256-unit tile with v_mfma_f32_32x32x16_bf16; each wave owns a 128 x 128
 // quarter (16 accumulator blocks, kept in the AGPRs). K advances in 32-wide
-// chunks through a 4-stage LDS ring filled by gfx950's global_load_lds (16
-// bytes per lane straight into LDS, no register staging), issued three chunks
-// ahead so HBM/MALL latency hides behind the MFMAs. Each wave's 128 units are
+// chunks through a 5-stage LDS ring filled by gfx950's global_load_lds (16
+// bytes per lane straight into LDS, no register staging), issued four chunks
+// ahead so HBM/MALL latency hides behind the MFMAs. Small batches use
+// gate_pack_skinny.hip instead (see launch_gate_pack). Each wave's 128 units are
 // whole TwELL tiles (T = 128 or 64), so every (token, tile) segment lives in
 // one wave and the packing needs no LDS round trip: in the accumulator layout
 // one register holds, across the 64 lanes, 32 consecutive units of two tokens,
@@ -343,6 +344,7 @@ __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }
 }  // namespace
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
+  if (a.M <= kSkinnyMaxM) return launch_gate_pack_skinny(a, s);
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.F + kBN - 1) / kBN;
   const dim3 grid(tiles_m * tiles_n), block(256);

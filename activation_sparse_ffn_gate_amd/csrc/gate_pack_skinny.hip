@@ -1,0 +1,273 @@
+// Gate GEMM with the TwELL packing in its epilogue, for small batches (decode).
+//
+// Same operation and outputs as gate_pack.hip (aimodeling.com TwELL summary,
+// paragraph 3; pulsen.vercel.app article, paragraph on tile matching; Tencent
+// Cloud article, section 2): z = x Wg^T, ReLU, per-(token, tile) counts,
+// ascending tile-local indices and fp32 values of the first C active units,
+// and the overflow list.
+//
+// With few tokens the 256 x 256 tiles of the large kernel leave most of the
+// chip idle (F / 256 workgroups) and each workgroup streams a megabyte of Wg
+// through one pipeline. Here a workgroup covers 32 tokens x 128 units (one
+// TwELL tile of 128, or two of 64) with 16 waves: 4 unit groups of 32 x 4
+// splits of every K chunk. K advances in 256-value chunks: every wave load
+// instruction reads 1 KB contiguous (two rows' 512-byte chunk), three chunks
+// are in flight in registers, and each chunk is stored to one of two LDS
+// stages (512-byte rows, 16-byte pieces XOR-swizzled by row mod 16) from which
+// the MFMA fragments are read. (Loading MFMA fragments straight from memory
+// makes every load instruction touch 32 rows, which ran at a fifth of this
+// rate.) The K splits meet through LDS in a fixed order.
+
+// Packing: per accumulator register a 64-bit ballot of z > 0 gives two tokens'
+// activity over the wave's 32 units; the waves of a tile exchange per-token
+// counts through LDS, so a unit's slot is the count in lower waves plus its
+// rank in its own ballot. Overflow rows join the same deduplicated list as in
+// the large kernel, and the last workgroup publishes n_ovf and clears the
+// control block.
+#include "twell_device.hpp"
+#include "twell_internal.hpp"
+
+namespace twell {
+namespace {
+
+constexpr int kSM = 32;    // tokens per workgroup
+constexpr int kSN = 128;   // units per workgroup
+constexpr int kKS = 4;     // K splits: waves per unit group
+constexpr int kWaves = 4 * kKS;
+constexpr int kKc = 256;   // K values per chunk: 512 bytes of every row
+constexpr int kRowB = 2 * kKc;
+constexpr int kStageB = (kSN + kSM) * kRowB;  // 80 KB: Wg rows, then x rows
+constexpr int kLdsB = 2 * kStageB;            // two stages
+
+// Byte offset of 16-byte piece p (0..31) of LDS row r: pieces are XOR-swizzled
+// with r mod 16, so the 16 rows a ds_read_b128 serves at once fall in 16
+// different bank groups.
+__device__ __forceinline__ uint32_t sk_off(int r, int p) {
+  return static_cast<uint32_t>(r * kRowB + ((p ^ (r & 15)) << 4));
+}
+
+template <int kT, bool kDebug>
+__global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateArgs a, int tiles_m) {
+  // One LDS object: two K-chunk stages; after the K loop its first bytes hold
+  // the K-split exchange, then the per-wave token counts and the finalize flag.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsB];
+  float(*s_red)[4][64][16] = reinterpret_cast<float(*)[4][64][16]>(smem);
+  int(*s_cnt)[kSM] = reinterpret_cast<int(*)[kSM]>(smem + (kKS - 1) * 4 * 64 * 16 * 4);
+  int* s_last = reinterpret_cast<int*>(smem + (kKS - 1) * 4 * 64 * 16 * 4 + 4 * kSM * 4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = w & 3, kh = w >> 2;  // unit group, K split
+  const int m0 = (blockIdx.x % tiles_m) * kSM;
+  const int n0 = (blockIdx.x / tiles_m) * kSN;
+  const int r = lane & 31, half = lane >> 5;
+
+  // Loads: every wave instruction reads 1 KB contiguous (two rows' 512-byte
+  // K chunk). Thread tid holds pieces q = tid + 1024 i of the chunk's
+  // (128 + 32) x 32 pieces: i < 4 Wg rows, i = 4 x rows. Rows past M or F read
+  // a valid row; their results are discarded. Offsets are 32-bit (x and Wg are
+  // below 2 GiB, checked by the host).
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const char* xb = reinterpret_cast<const char*>(a.x);
+  const char* wb = reinterpret_cast<const char*>(a.Wg);
+  uint32_t goff[5], soff[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int q = tid + 1024 * i;
+    const int row = q >> 5, piece = q & 31;  // row 0..127 Wg, 128..159 x
+    const int grow = (row < kSN) ? min(n0 + row, a.F - 1) : min(m0 + row - kSN, a.M - 1);
+    goff[i] = static_cast<uint32_t>(grow) * row_bytes + static_cast<uint32_t>(piece) * 16u;
+    soff[i] = sk_off(row, piece);
+  }
+  struct Regs {
+    u32x4_t v[5];
+  };
+  auto gload = [&](Regs& g, int ck) {
+    const uint32_t k = static_cast<uint32_t>(ck) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+      g.v[i] = *reinterpret_cast<const u32x4_t*>((i < 4 ? wb : xb) + goff[i] + k);
+  };
+  auto sstore = [&](const Regs& g, int st) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) lds_store16(smem + st * kStageB, soff[i], g.v[i]);
+  };
+
+  // MFMA: wave (wn, kh) takes units wn*32 .. +31 and k-steps kh*4 .. +3 of the
+  // chunk's 16; step s uses piece 2s + half of its rows (A: token, B: unit).
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  auto mma = [&](int st) {
+    const uint8_t* base = smem + st * kStageB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = 2 * (kh * 4 + j) + half;
+      const u32x4_t bf = lds_load16(base, sk_off(wn * 32 + r, p));
+      const u32x4_t af = lds_load16(base, sk_off(kSN + r, p));
+      acc = mfma_32x32x16(af, bf, acc);
+    }
+  };
+
+  // Three chunks in flight in registers, two LDS stages. Chunk c: wait for its
+  // registers, store them to stage c % 2, barrier (every wave is past chunk
+  // c - 2's reads of that stage, and chunk c is visible), issue the loads of
+  // chunk c + 3, then the products. Loads past the last chunk re-read it
+  // (unconditional loads keep the wait counts exact).
+  const int nck = a.d / kKc;
+  Regs g0, g1, g2;
+  gload(g0, 0);
+  gload(g1, min(1, nck - 1));
+  gload(g2, min(2, nck - 1));
+  for (int ck = 0; ck < nck; ck += 3) {
+    sstore(g0, ck & 1);
+    __syncthreads();
+    gload(g0, min(ck + 3, nck - 1));
+    mma(ck & 1);
+    if (ck + 1 < nck) {  // uniform
+      sstore(g1, (ck + 1) & 1);
+      __syncthreads();
+      gload(g1, min(ck + 4, nck - 1));
+      mma((ck + 1) & 1);
+    }
+    if (ck + 2 < nck) {
+      sstore(g2, (ck + 2) & 1);
+      __syncthreads();
+      gload(g2, min(ck + 5, nck - 1));
+      mma((ck + 2) & 1);
+    }
+  }
+  __syncthreads();  // every wave is done with the stages
+
+  // K splits: splits 1 .. kKS-1 hand their sums to split 0, which adds them in
+  // split order.
+  if (kh > 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_red[kh - 1][wn][lane][v] = acc[v];
+  }
+  __syncthreads();
+
+  const int nT = a.F / kT;
+  const int C = a.C;
+  constexpr int kWavesPerTile = kT / 32;     // 4 (T = 128) or 2 (T = 64)
+  const int tile = (n0 + wn * 32) / kT;       // this wave's TwELL tile
+  const int wt = wn % kWavesPerTile;          // its rank among the tile's waves
+  uint32_t* flags = a.ctrl + kCtrlBytes / 4;
+  int appended = 0;
+
+  if (kh == 0) {
+#pragma unroll
+    for (int j = 0; j < kKS - 1; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] += s_red[j][wn][lane][v];
+    const int ucol = n0 + wn * 32 + r;  // this lane's unit
+    const bool unit_ok = ucol < a.F;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = unit_ok && m0 + acc_row(v, half) < a.M;
+      if constexpr (kDebug) {
+        if (ok) a.z_debug[static_cast<size_t>(m0 + acc_row(v, half)) * a.F + ucol] = acc[v];
+      }
+      acc[v] = ok ? acc[v] : 0.f;  // rows and units past the matrix never count
+    }
+    // This wave's count of each of the 32 tokens, lane t holding token t.
+    uint64_t bal[16];
+    int cw = 0;
+    static_for<0, 16>([&](auto I) {
+      constexpr int v = decltype(I)::value;
+      bal[v] = __ballot(acc[v] > 0.f);
+      cw = writelane<acc_row(v, 0)>(cw, __popc(static_cast<uint32_t>(bal[v])));
+      cw = writelane<acc_row(v, 1)>(cw, __popc(static_cast<uint32_t>(bal[v] >> 32)));
+    });
+    if (lane < kSM) s_cnt[wn][lane] = cw;
+    __syncthreads();  // (1) counts of every wave
+    // Lane t: active units of token t in the tile's lower waves, and in all of them.
+    int pre = 0, tot = 0;
+    const int wfirst = wn - wt;
+#pragma unroll
+    for (int j = 0; j < kWavesPerTile; ++j) {
+      const int c = s_cnt[wfirst + j][lane & 31];
+      tot += c;
+      pre += (j < wt) ? c : 0;
+    }
+    if (tile < nT) {
+      const uint32_t row_slots = static_cast<uint32_t>(nT * C);
+      const uint32_t ulocal = static_cast<uint32_t>(wt * 32 + r);  // index inside the tile
+      static_for<0, 16>([&](auto I) {
+        constexpr int v = decltype(I)::value;
+        const uint64_t bq = bal[v];
+        if (bq == 0) return;
+        const int t_lo = acc_row(v, 0), t_hi = acc_row(v, 1);
+        const uint32_t pre_lo = __builtin_amdgcn_readlane(pre, t_lo);
+        const uint32_t pre_hi = __builtin_amdgcn_readlane(pre, t_hi);
+        const uint32_t rank = half ? __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32), 0u)
+                                   : __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bq), 0u);
+        const uint32_t slot = rank + (half ? pre_hi : pre_lo);
+        if (acc[v] > 0.f && slot < static_cast<uint32_t>(C)) {
+          const uint32_t row = static_cast<uint32_t>(m0 + acc_row(v, half));
+          const uint32_t at = row * row_slots + static_cast<uint32_t>(tile * C) + slot;
+          store_at(a.vals, at * 4u, acc[v]);
+          store_at(a.idx, at, static_cast<uint8_t>(ulocal));
+        }
+      });
+      // Counts and overflow membership: the tile's first wave, lane t = token t.
+      const int row = m0 + lane;
+      if (wt == 0 && lane < kSM && row < a.M) {
+        a.counts[static_cast<size_t>(row) * nT + tile] = static_cast<uint16_t>(tot);
+        if (tot > C && atomicExch(&flags[row], 1u) == 0u) {
+          appended = 1;
+          const uint32_t pos = atomicAdd(&a.ctrl[0], 1u);
+          if (pos < static_cast<uint32_t>(a.M))
+            __hip_atomic_store(&a.ovf_rows[pos], row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  } else {
+    __syncthreads();  // (1)
+  }
+
+  // Finalize as in the large kernel: waves that appended release their list
+  // entries; the last workgroup publishes n_ovf and clears the control block.
+  if (__ballot(appended) != 0) __threadfence();
+  raw_barrier();
+  if (tid == 0) {
+    const uint32_t done = atomicAdd(&a.ctrl[1], 1u);
+    *s_last = (done == static_cast<uint32_t>(gridDim.x) - 1u);
+  }
+  waitcnt<63, 0>();
+  raw_barrier();
+  if (*s_last) {
+    __threadfence();
+    uint32_t n = __hip_atomic_load(&a.ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    n = min(n, static_cast<uint32_t>(a.M));
+    for (uint32_t i = tid; i < n; i += blockDim.x) {
+      const int rr = __hip_atomic_load(&a.ovf_rows[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (rr >= 0 && rr < a.M) __hip_atomic_store(&flags[rr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) {
+      *a.n_ovf = static_cast<int32_t>(n);
+      __hip_atomic_store(&a.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s) {
+  const int tiles_m = (a.M + kSM - 1) / kSM;
+  const int tiles_n = (a.F + kSN - 1) / kSN;
+  const dim3 grid(tiles_m * tiles_n), block(64 * kWaves);
+  const bool dbg = a.z_debug != nullptr;
+  if (a.T == 128) {
+    if (dbg) gate_pack_skinny_kernel<128, true><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<128, false><<<grid, block, 0, s>>>(a, tiles_m);
+  } else {
+    if (dbg) gate_pack_skinny_kernel<64, true><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<64, false><<<grid, block, 0, s>>>(a, tiles_m);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace twell

@@ -85,6 +85,9 @@ struct SlicedLayout {
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+// Batches up to this many tokens take the small-batch gate kernel.
+constexpr int kSkinnyMaxM = 256;
+hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s);
 hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 // d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
 bool sliced_supports(int64_t d, int64_t F);

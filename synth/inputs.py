@@ -107,6 +107,20 @@ WORKLOADS: dict[str, Workload] = {
 for _w in sweep_workloads():
     WORKLOADS[_w.name] = _w
 
+DECODE_BATCHES = (1, 16, 64, 256)
+
+
+def decode_workloads() -> list[Workload]:
+    """The 1.5B-like layer at small batches (decode / batched decode)."""
+    return [
+        _uniform(f"decode_m{m}", m, 2048, 8192, 128, 16, 29 / 8192, 1050 + i)
+        for i, m in enumerate(DECODE_BATCHES)
+    ]
+
+
+for _w in decode_workloads():
+    WORKLOADS[_w.name] = _w
+
 
 def scaled(w: Workload, **changes) -> Workload:
     """Same density structure at other sizes (for oracle-sized parity cases).

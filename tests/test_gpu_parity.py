@@ -49,7 +49,7 @@ SMALL = {
     "fused_only_d2304": scaled(WORKLOADS["ffn1p5b"], M=200, d=2304, F=1024, mean_nnz=12.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
-    k for k in WORKLOADS if k.startswith("sweep_")
+    k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
 ]
 
 
@@ -256,7 +256,7 @@ def test_full_size(name):
 
     # sampled rows: active sets and y against the fp64 definition
     rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([rng.choice(w.M, 96, replace=False), view["ovf"][:32]]))
+    rows = np.unique(np.concatenate([rng.choice(w.M, min(96, w.M), replace=False), view["ovf"][:32]]))
     rms = np.sqrt(sum(np.square(O.gate_preactivations(inp.x, inp.Wg, rows=np.arange(s, min(s + 2048, w.M)))).sum(axis=0)
                       for s in range(0, w.M, 2048)) / w.M)
     Zs = O.gate_preactivations(inp.x, inp.Wg, rows=rows)
