@@ -159,8 +159,8 @@ def dense_torch(x, Wg, WuT, Wd):
     return run
 
 
-def density_sweep(dev, steps, warmup):
-    """Sparse forward vs the dense baselines at every sweep density."""
+def layer_sweep(dev, names, steps, warmup):
+    """Sparse forward vs the dense baselines on each named layer."""
     import numpy as np
     import torch
 
@@ -168,7 +168,7 @@ def density_sweep(dev, steps, warmup):
     from synth import WORKLOADS, make_inputs
 
     out = []
-    for name in sorted((k for k in WORKLOADS if k.startswith("sweep_")), key=lambda k: WORKLOADS[k].mean_nnz):
+    for name in names:
         w = WORKLOADS[name]
         inp = make_inputs(w)
         x, Wg, WuT, Wd = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -191,6 +191,7 @@ def density_sweep(dev, steps, warmup):
             "workload": name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C,
             "active_pct": round(100.0 * counts.sum() / (w.M * w.F), 3),
             "overflow_rows": int(view.n_ovf.item()),
+            "sparse_tokens_per_s": round(w.M / (res["sparse"] * 1e-3), 1),
             "sparse_ms": round(res["sparse"], 5), "dense_ms": round(res["dense"], 5),
             "dense_hipblaslt_ms": round(res["dense_hipblaslt"], 5),
             "speedup_vs_dense": round(res["dense"] / res["sparse"], 3),
@@ -397,7 +398,12 @@ def main():
         },
     }
     if not args.no_sweep:  # HBM holds both layers' buffers easily
-        out["density_sweep"] = density_sweep(dev, args.sweep_steps, 2)
+        from synth import WORKLOADS as _W
+
+        sweep = sorted((k for k in _W if k.startswith("sweep_")), key=lambda k: _W[k].mean_nnz)
+        out["density_sweep"] = layer_sweep(dev, sweep, args.sweep_steps, 2)
+        decode = sorted((k for k in _W if k.startswith("decode_")), key=lambda k: _W[k].M)
+        out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))

@@ -121,7 +121,8 @@ def test_components_compose(name):
     p = tw.gate_pack(x, Wg, w.T, w.C)
     g = host_packing(p)
     assert np.array_equal(view["counts"], g["counts"]) and np.array_equal(view["ovf"], g["ovf"])
-    updown = tw.sliced_updown if sliced_ok(w.d) else tw.fused_updown
+    # the forward's choice: the sliced form from 16 rows on, where d allows it
+    updown = tw.sliced_updown if (w.M >= 16 and sliced_ok(w.d)) else tw.fused_updown
     y = updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
     yh = y.cpu().numpy()
     ovf = g["ovf"]
