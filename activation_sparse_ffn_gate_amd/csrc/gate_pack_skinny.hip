@@ -30,30 +30,44 @@
 namespace twell {
 namespace {
 
-constexpr int kSM = 32;    // tokens per workgroup
 constexpr int kSN = 128;   // units per workgroup
 constexpr int kKS = 4;     // K splits: waves per unit group
 constexpr int kWaves = 4 * kKS;
-constexpr int kKc = 256;   // K values per chunk: 512 bytes of every row
-constexpr int kRowB = 2 * kKc;
-constexpr int kStageB = (kSN + kSM) * kRowB;  // 80 KB: Wg rows, then x rows
-constexpr int kLdsB = 2 * kStageB;            // two stages
 
-// Byte offset of 16-byte piece p (0..31) of LDS row r: pieces are XOR-swizzled
-// with r mod 16, so the 16 rows a ds_read_b128 serves at once fall in 16
-// different bank groups.
+// RB blocks of 32 tokens per workgroup; K chunk of KC values (KC / 8 pieces of
+// 16 bytes per row) so that two stages of (128 + 32 RB) rows fit in LDS.
+template <int RB>
+struct SkinnyShape {
+  static constexpr int kSM = 32 * RB;
+  static constexpr int kKc = RB == 1 ? 256 : 128;
+  static constexpr int kPieces = kKc / 8;
+  static constexpr int kRowB = 2 * kKc;
+  static constexpr int kRows = kSN + kSM;
+  static constexpr int kStageB = kRows * kRowB;
+  static constexpr int kLoads = kRows * kPieces / (64 * kWaves);  // 16-byte loads per thread per chunk
+  static constexpr int kRedB = (kKS - 1) * 4 * 64 * 16 * RB * 4;
+  static constexpr int kLdsB = (2 * kStageB > kRedB + 4 * kSM * 4 + 16) ? 2 * kStageB : kRedB + 4 * kSM * 4 + 16;
+  static_assert(kRows * kPieces % (64 * kWaves) == 0, "whole loads per thread");
+};
+
+// Byte offset of 16-byte piece p of LDS row r (rows of kRowB bytes): pieces are
+// XOR-swizzled with r mod 16, so the 16 rows a ds_read_b128 serves at once fall
+// in 16 different bank groups.
+template <int kRowB>
 __device__ __forceinline__ uint32_t sk_off(int r, int p) {
   return static_cast<uint32_t>(r * kRowB + ((p ^ (r & 15)) << 4));
 }
 
-template <int kT, bool kDebug>
+template <int kT, bool kDebug, int RB>
 __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateArgs a, int tiles_m) {
+  using S = SkinnyShape<RB>;
+  constexpr int kSM = S::kSM;
   // One LDS object: two K-chunk stages; after the K loop its first bytes hold
   // the K-split exchange, then the per-wave token counts and the finalize flag.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsB];
-  float(*s_red)[4][64][16] = reinterpret_cast<float(*)[4][64][16]>(smem);
-  int(*s_cnt)[kSM] = reinterpret_cast<int(*)[kSM]>(smem + (kKS - 1) * 4 * 64 * 16 * 4);
-  int* s_last = reinterpret_cast<int*>(smem + (kKS - 1) * 4 * 64 * 16 * 4 + 4 * kSM * 4);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsB];
+  float(*s_red)[4][64][16 * RB] = reinterpret_cast<float(*)[4][64][16 * RB]>(smem);
+  int(*s_cnt)[kSM] = reinterpret_cast<int(*)[kSM]>(smem + S::kRedB);
+  int* s_last = reinterpret_cast<int*>(smem + S::kRedB + 4 * kSM * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -63,50 +77,59 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   const int n0 = (blockIdx.x / tiles_m) * kSN;
   const int r = lane & 31, half = lane >> 5;
 
-  // Loads: every wave instruction reads 1 KB contiguous (two rows' 512-byte
-  // K chunk). Thread tid holds pieces q = tid + 1024 i of the chunk's
-  // (128 + 32) x 32 pieces: i < 4 Wg rows, i = 4 x rows. Rows past M or F read
-  // a valid row; their results are discarded. Offsets are 32-bit (x and Wg are
-  // below 2 GiB, checked by the host).
+  // Loads: every wave instruction reads 1 KB contiguous (whole rows' K chunk).
+  // Thread tid holds pieces q = tid + 1024 i of the chunk's kRows x kPieces:
+  // rows below 128 are Wg rows, the rest x rows. Rows past M or F read a valid
+  // row; their results are discarded. Offsets are 32-bit (x and Wg are below
+  // 2 GiB, checked by the host).
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
   const char* xb = reinterpret_cast<const char*>(a.x);
   const char* wb = reinterpret_cast<const char*>(a.Wg);
-  uint32_t goff[5], soff[5];
+  uint32_t goff[S::kLoads], soff[S::kLoads];
+  bool isw[S::kLoads];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int q = tid + 1024 * i;
-    const int row = q >> 5, piece = q & 31;  // row 0..127 Wg, 128..159 x
-    const int grow = (row < kSN) ? min(n0 + row, a.F - 1) : min(m0 + row - kSN, a.M - 1);
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int q = tid + 64 * kWaves * i;
+    const int row = q / S::kPieces, piece = q % S::kPieces;
+    isw[i] = row < kSN;
+    const int grow = isw[i] ? min(n0 + row, a.F - 1) : min(m0 + row - kSN, a.M - 1);
     goff[i] = static_cast<uint32_t>(grow) * row_bytes + static_cast<uint32_t>(piece) * 16u;
-    soff[i] = sk_off(row, piece);
+    soff[i] = sk_off<S::kRowB>(row, piece);
   }
   struct Regs {
-    u32x4_t v[5];
+    u32x4_t v[S::kLoads];
   };
   auto gload = [&](Regs& g, int ck) {
-    const uint32_t k = static_cast<uint32_t>(ck) * kRowB;
+    const uint32_t k = static_cast<uint32_t>(ck) * S::kRowB;
 #pragma unroll
-    for (int i = 0; i < 5; ++i)
-      g.v[i] = *reinterpret_cast<const u32x4_t*>((i < 4 ? wb : xb) + goff[i] + k);
+    for (int i = 0; i < S::kLoads; ++i)
+      g.v[i] = *reinterpret_cast<const u32x4_t*>((isw[i] ? wb : xb) + goff[i] + k);
   };
   auto sstore = [&](const Regs& g, int st) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) lds_store16(smem + st * kStageB, soff[i], g.v[i]);
+    for (int i = 0; i < S::kLoads; ++i) lds_store16(smem + st * S::kStageB, soff[i], g.v[i]);
   };
 
-  // MFMA: wave (wn, kh) takes units wn*32 .. +31 and k-steps kh*4 .. +3 of the
-  // chunk's 16; step s uses piece 2s + half of its rows (A: token, B: unit).
-  f32x16_t acc;
+  // MFMA: wave (wn, kh) takes units wn*32 .. +31 and a quarter of the chunk's
+  // kKc / 16 k-steps; step s uses piece 2s + half of its rows (A: token rows,
+  // one accumulator block per 32 tokens; B: unit rows).
+  constexpr int kStepsPerWave = S::kKc / 16 / kKS;
+  f32x16_t acc[RB];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
   auto mma = [&](int st) {
-    const uint8_t* base = smem + st * kStageB;
+    const uint8_t* base = smem + st * S::kStageB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = 2 * (kh * 4 + j) + half;
-      const u32x4_t bf = lds_load16(base, sk_off(wn * 32 + r, p));
-      const u32x4_t af = lds_load16(base, sk_off(kSN + r, p));
-      acc = mfma_32x32x16(af, bf, acc);
+    for (int j = 0; j < kStepsPerWave; ++j) {
+      const int p = 2 * (kh * kStepsPerWave + j) + half;
+      const u32x4_t bf = lds_load16(base, sk_off<S::kRowB>(wn * 32 + r, p));
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const u32x4_t af = lds_load16(base, sk_off<S::kRowB>(kSN + 32 * b + r, p));
+        acc[b] = mfma_32x32x16(af, bf, acc[b]);
+      }
     }
   };
 
@@ -115,7 +138,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   // c - 2's reads of that stage, and chunk c is visible), issue the loads of
   // chunk c + 3, then the products. Loads past the last chunk re-read it
   // (unconditional loads keep the wait counts exact).
-  const int nck = a.d / kKc;
+  const int nck = a.d / S::kKc;
   Regs g0, g1, g2;
   gload(g0, 0);
   gload(g1, min(1, nck - 1));
@@ -144,7 +167,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   // split order.
   if (kh > 0) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s_red[kh - 1][wn][lane][v] = acc[v];
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_red[kh - 1][wn][lane][16 * b + v] = acc[b][v];
   }
   __syncthreads();
 
@@ -160,25 +185,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
 #pragma unroll
     for (int j = 0; j < kKS - 1; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] += s_red[j][wn][lane][v];
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] += s_red[j][wn][lane][16 * b + v];
     const int ucol = n0 + wn * 32 + r;  // this lane's unit
     const bool unit_ok = ucol < a.F;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const bool ok = unit_ok && m0 + acc_row(v, half) < a.M;
-      if constexpr (kDebug) {
-        if (ok) a.z_debug[static_cast<size_t>(m0 + acc_row(v, half)) * a.F + ucol] = acc[v];
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 32 * b + acc_row(v, half);
+        const bool ok = unit_ok && row < a.M;
+        if constexpr (kDebug) {
+          if (ok) a.z_debug[static_cast<size_t>(row) * a.F + ucol] = acc[b][v];
+        }
+        acc[b][v] = ok ? acc[b][v] : 0.f;  // rows and units past the matrix never count
       }
-      acc[v] = ok ? acc[v] : 0.f;  // rows and units past the matrix never count
-    }
-    // This wave's count of each of the 32 tokens, lane t holding token t.
-    uint64_t bal[16];
+    // This wave's count of each token, lane t holding token t (t < kSM).
+    uint64_t bal[RB][16];
     int cw = 0;
-    static_for<0, 16>([&](auto I) {
-      constexpr int v = decltype(I)::value;
-      bal[v] = __ballot(acc[v] > 0.f);
-      cw = writelane<acc_row(v, 0)>(cw, __popc(static_cast<uint32_t>(bal[v])));
-      cw = writelane<acc_row(v, 1)>(cw, __popc(static_cast<uint32_t>(bal[v] >> 32)));
+    static_for<0, 16 * RB>([&](auto I) {
+      constexpr int b = decltype(I)::value / 16, v = decltype(I)::value % 16;
+      bal[b][v] = __ballot(acc[b][v] > 0.f);
+      cw = writelane<32 * b + acc_row(v, 0)>(cw, __popc(static_cast<uint32_t>(bal[b][v])));
+      cw = writelane<32 * b + acc_row(v, 1)>(cw, __popc(static_cast<uint32_t>(bal[b][v] >> 32)));
     });
     if (lane < kSM) s_cnt[wn][lane] = cw;
     __syncthreads();  // (1) counts of every wave
@@ -187,27 +217,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
     const int wfirst = wn - wt;
 #pragma unroll
     for (int j = 0; j < kWavesPerTile; ++j) {
-      const int c = s_cnt[wfirst + j][lane & 31];
+      const int c = s_cnt[wfirst + j][lane % kSM];
       tot += c;
       pre += (j < wt) ? c : 0;
     }
     if (tile < nT) {
       const uint32_t row_slots = static_cast<uint32_t>(nT * C);
       const uint32_t ulocal = static_cast<uint32_t>(wt * 32 + r);  // index inside the tile
-      static_for<0, 16>([&](auto I) {
-        constexpr int v = decltype(I)::value;
-        const uint64_t bq = bal[v];
+      static_for<0, 16 * RB>([&](auto I) {
+        constexpr int b = decltype(I)::value / 16, v = decltype(I)::value % 16;
+        const uint64_t bq = bal[b][v];
         if (bq == 0) return;
-        const int t_lo = acc_row(v, 0), t_hi = acc_row(v, 1);
+        constexpr int t_lo = 32 * b + acc_row(v, 0), t_hi = 32 * b + acc_row(v, 1);
         const uint32_t pre_lo = __builtin_amdgcn_readlane(pre, t_lo);
         const uint32_t pre_hi = __builtin_amdgcn_readlane(pre, t_hi);
         const uint32_t rank = half ? __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32), 0u)
                                    : __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bq), 0u);
         const uint32_t slot = rank + (half ? pre_hi : pre_lo);
-        if (acc[v] > 0.f && slot < static_cast<uint32_t>(C)) {
-          const uint32_t row = static_cast<uint32_t>(m0 + acc_row(v, half));
+        if (acc[b][v] > 0.f && slot < static_cast<uint32_t>(C)) {
+          const uint32_t row = static_cast<uint32_t>(m0 + 32 * b + acc_row(v, half));
           const uint32_t at = row * row_slots + static_cast<uint32_t>(tile * C) + slot;
-          store_at(a.vals, at * 4u, acc[v]);
+          store_at(a.vals, at * 4u, acc[b][v]);
           store_at(a.idx, at, static_cast<uint8_t>(ulocal));
         }
       });
@@ -253,21 +283,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   }
 }
 
-}  // namespace
-
-hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s) {
-  const int tiles_m = (a.M + kSM - 1) / kSM;
+template <int RB>
+hipError_t launch_rb(const GateArgs& a, hipStream_t s) {
+  const int tiles_m = (a.M + 32 * RB - 1) / (32 * RB);
   const int tiles_n = (a.F + kSN - 1) / kSN;
   const dim3 grid(tiles_m * tiles_n), block(64 * kWaves);
   const bool dbg = a.z_debug != nullptr;
   if (a.T == 128) {
-    if (dbg) gate_pack_skinny_kernel<128, true><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_skinny_kernel<128, false><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_skinny_kernel<128, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<128, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
   } else {
-    if (dbg) gate_pack_skinny_kernel<64, true><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_skinny_kernel<64, false><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_skinny_kernel<64, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<64, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s) {
+  // 32-token tiles while they already give a few hundred workgroups' worth of
+  // parallelism; 64-token tiles (half the re-reads of Wg) above.
+  return a.M <= kSkinnyRb1MaxM ? launch_rb<1>(a, s) : launch_rb<2>(a, s);
 }
 
 }  // namespace twell

@@ -87,6 +87,7 @@ struct SlicedLayout {
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
 // Batches up to this many tokens take the small-batch gate kernel.
 constexpr int kSkinnyMaxM = 256;
+constexpr int kSkinnyRb1MaxM = 128;  // up to here 32-token tiles, then 64-token tiles
 hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s);
 hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 // d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
