@@ -151,6 +151,147 @@ __global__ __launch_bounds__(256) void fused_updown_kernel(FusedArgs a) {
   }
 }
 
+// Few tokens: one workgroup of kWideWaves waves per token, so a token's units
+// are not walked by a single wave in a chain of dependent load rounds. The
+// waves build the token's (unit, value) list together, then
+//   up:   wave w takes list entries in chunks of UP (chunk c goes to wave
+//         c mod kWideWaves), computes u_j exactly as above (same lane layout of
+//         x, same reduction) and leaves h_j = g_j * u_j in the list;
+//   down: wave w, lane l owns the 4-column groups q = 64 w + l (+ 64 kWideWaves
+//         i); every wave walks the whole list in order, DN units' Wd loads in
+//         flight at a time, and adds h_j * Wd[j] to its columns.
+// A wave reads a round's entries with one LDS load, lane u holding entry u,
+// and takes each unit's index and value from lane u with v_readlane.
+// Every product and every per-column sum is taken in the same order as in the
+// one-wave form, so both forms give the same bits.
+constexpr int kWideWaves = 8;
+constexpr int kWideCap = 1024;  // list entries per round
+
+template <int VEC, int NCH, int UP, int NQ, int DN>
+__global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(FusedArgs a) {
+  using LoadT = typename Vec<VEC>::T;
+  constexpr int kW = Vec<VEC>::kWords;
+  constexpr int kChunk = 64 * VEC;
+
+  __shared__ int s_j[kWideCap];
+  __shared__ float s_h[kWideCap];  // gate value, then h
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x;
+
+  const int nT = a.F / a.T;
+  const int C = a.C;
+  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
+
+  // Every wave reads the counts, so all of them take the same decision.
+  bool over = false;
+  for (int t = lane; t < nT; t += 64) over |= cnt_row[t] > C;
+  if (__ballot(over) != 0) return;  // overflow row: owned by the dense fallback
+
+  LoadT xv[NCH];
+  const uint16_t* xr = a.x + static_cast<size_t>(row) * a.d + lane * VEC;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) xv[ch] = *reinterpret_cast<const LoadT*>(xr + ch * kChunk);
+
+  const int quads = a.d / 4;  // multiple of 64: the guard below is wave-uniform
+  float acc[NQ][4];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[i][k] = 0.f;
+
+  const int tmask = a.T - 1;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const char* wdb = reinterpret_cast<const char*>(a.Wd);
+
+  for (int t0 = 0; t0 < nT; t0 += 64) {
+    const int t = t0 + lane;
+    const int c = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
+    const int incl = wave_inclusive_scan(c);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    const int off = incl - c;
+    const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
+    for (int base = 0; base < total; base += kWideCap) {
+      // Fill: lane t of wave w copies slots s = s_lo + w, s_lo + w + kWideWaves, ...
+      const int s_lo = max(0, base - off);
+      const int s_hi = min(c, base + kWideCap - off);
+      for (int s = s_lo + w; s < s_hi; s += kWideWaves) {
+        s_j[off + s - base] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
+        s_h[off + s - base] = a.vals[slot0 + s];
+      }
+      __syncthreads();
+      const int n = min(kWideCap, total - base);
+
+      // Up: chunks of UP entries round-robin over the waves.
+      for (int e0 = w * UP; e0 < n; e0 += kWideWaves * UP) {
+        // lane u holds entry e0 + u (the last entry for lanes past the list)
+        const int jv = s_j[min(e0 + min(lane, UP - 1), n - 1)];
+        const float gv = s_h[min(e0 + min(lane, UP - 1), n - 1)];
+        LoadT wu[UP][NCH];
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          const int ju = __builtin_amdgcn_readlane(jv, u);
+          const uint16_t* pu = a.WuT + static_cast<size_t>(ju) * a.d + lane * VEC;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) wu[u][ch] = *reinterpret_cast<const LoadT*>(pu + ch * kChunk);
+        }
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+          float part = 0.f;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+            for (int q = 0; q < kW; ++q) part = dot2_bf16(xv[ch][q], wu[u][ch][q], part);
+          const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), u)) * wave_sum(part);
+          if (e0 + u < n && lane == 0) s_h[e0 + u] = h;
+        }
+      }
+      __syncthreads();
+
+      // Down: the whole list in order, DN entries' loads at a time.
+      for (int e0 = 0; e0 < n; e0 += DN) {
+        const int jv = s_j[min(e0 + min(lane, DN - 1), n - 1)];
+        const float hv = s_h[min(e0 + min(lane, DN - 1), n - 1)];
+        u32x2_t wd[DN][NQ];
+#pragma unroll
+        for (int u = 0; u < DN; ++u) {
+          const size_t rb = static_cast<size_t>(__builtin_amdgcn_readlane(jv, u)) * row_bytes;
+#pragma unroll
+          for (int i = 0; i < NQ; ++i) {
+            const int q = (i * kWideWaves + w) * 64 + lane;
+            if (q < quads) wd[u][i] = *reinterpret_cast<const u32x2_t*>(wdb + rb + static_cast<uint32_t>(q) * 8u);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < DN; ++u) {
+          if (e0 + u < n) {  // uniform
+            const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), u));
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+              if ((i * kWideWaves + w) * 64 < quads) {  // uniform
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  acc[i][2 * q] = fmaf(h, bf16_lo(wd[u][i][q]), acc[i][2 * q]);
+                  acc[i][2 * q + 1] = fmaf(h, bf16_hi(wd[u][i][q]), acc[i][2 * q + 1]);
+                }
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();  // the list is refilled next round
+    }
+  }
+
+  float* yr = a.y + static_cast<size_t>(row) * a.d;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = (i * kWideWaves + w) * 64 + lane;
+    if (q < quads) *reinterpret_cast<float4*>(yr + 4 * q) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+}
+
 template <int NCH>
 constexpr int unroll_for() {
 #ifdef TWELL_FUSED_UNROLL
@@ -162,6 +303,16 @@ constexpr int unroll_for() {
 
 template <int VEC, int NCH>
 hipError_t launch_vec(const FusedArgs& a, hipStream_t s) {
+  if (a.M < kFewRows) {
+    // d = 64 * VEC * NCH; NQ 4-column groups per lane cover it with 8 waves
+    constexpr int kD = 64 * VEC * NCH;
+    constexpr int kNQ = (kD / 4 + 64 * kWideWaves - 1) / (64 * kWideWaves);
+    // entries per up round per wave / per down round: as deep as registers allow
+    constexpr int kUp = NCH <= 2 ? 8 : (NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1));
+    constexpr int kDn = kNQ == 1 ? 64 : (kNQ == 2 ? 24 : 8);
+    fused_updown_wide_kernel<VEC, NCH, kUp, kNQ, kDn><<<dim3(a.M), dim3(64 * kWideWaves), 0, s>>>(a);
+    return hipGetLastError();
+  }
   const dim3 grid((a.M + kRowsPerWG - 1) / kRowsPerWG), block(64 * kRowsPerWG);
   fused_updown_kernel<VEC, NCH, unroll_for<NCH>()><<<grid, block, 0, s>>>(a);
   return hipGetLastError();

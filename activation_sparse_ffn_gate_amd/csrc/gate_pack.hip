@@ -26,6 +26,7 @@
 // device-scope atomics. The last workgroup to finish publishes the list length
 // and clears the dedup flags, so the control block is zero again when the
 // kernel ends and no separate clearing launch is needed.
+#include "gate_overflow.hpp"
 #include "twell_device.hpp"
 #include "twell_internal.hpp"
 
@@ -284,7 +285,6 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 
   // Counts: lane L writes tokens wrow0 + L and wrow0 + 64 + L; overflow rows
   // join the set.
-  uint32_t* flags = a.ctrl + kCtrlBytes / 4;
   int appended = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -298,45 +298,13 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
           over |= cnt[tt][h] > C;
         }
       }
-      if (over && atomicExch(&flags[row], 1u) == 0u) {
-        appended = 1;
-        const uint32_t pos = atomicAdd(&a.ctrl[0], 1u);
-        // pos < M whenever the control block started zeroed, as the API requires
-        if (pos < static_cast<uint32_t>(a.M))
-          __hip_atomic_store(&a.ovf_rows[pos], row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (over) appended |= overflow_append(a, row);
     }
   }
 
-  // The last workgroup publishes n_ovf and clears the control block. Only the
-  // waves that appended rows have list entries to release to it: each of them
-  // releases its own (the fence waits for that wave's stores); the other waves
-  // go on without waiting for their packing stores to drain, so the barriers
-  // below carry no memory fence. The stage buffers are idle now and hold the
-  // workgroup's flag.
-  int* sflag = reinterpret_cast<int*>(smem);  // [0] = this workgroup finished last
-  if (__ballot(appended) != 0) __threadfence();
-  raw_barrier();  // every wave is past its appends (and their release) and done with LDS
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(&a.ctrl[1], 1u);
-    sflag[0] = (done == static_cast<uint32_t>(gridDim.x) - 1u);
-  }
-  waitcnt<63, 0>();  // the flag store has reached LDS
-  raw_barrier();
-  if (sflag[0]) {
-    __threadfence();
-    uint32_t n = __hip_atomic_load(&a.ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    n = min(n, static_cast<uint32_t>(a.M));
-    for (uint32_t i = tid; i < n; i += 256) {
-      const int r = __hip_atomic_load(&a.ovf_rows[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (r >= 0 && r < a.M) __hip_atomic_store(&flags[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == 0) {
-      *a.n_ovf = static_cast<int32_t>(n);
-      __hip_atomic_store(&a.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  // The last workgroup publishes n_ovf and clears the control block; the
+  // stage buffers are idle now and hold its flag.
+  overflow_finalize(a, appended, reinterpret_cast<int*>(smem));
 }
 
 __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }

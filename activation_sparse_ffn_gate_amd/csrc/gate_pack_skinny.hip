@@ -24,6 +24,7 @@
 // rank in its own ballot. Overflow rows join the same deduplicated list as in
 // the large kernel, and the last workgroup publishes n_ovf and clears the
 // control block.
+#include "gate_overflow.hpp"
 #include "twell_device.hpp"
 #include "twell_internal.hpp"
 
@@ -178,7 +179,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   constexpr int kWavesPerTile = kT / 32;     // 4 (T = 128) or 2 (T = 64)
   const int tile = (n0 + wn * 32) / kT;       // this wave's TwELL tile
   const int wt = wn % kWavesPerTile;          // its rank among the tile's waves
-  uint32_t* flags = a.ctrl + kCtrlBytes / 4;
   int appended = 0;
 
   if (kh == 0) {
@@ -245,42 +245,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
       const int row = m0 + lane;
       if (wt == 0 && lane < kSM && row < a.M) {
         a.counts[static_cast<size_t>(row) * nT + tile] = static_cast<uint16_t>(tot);
-        if (tot > C && atomicExch(&flags[row], 1u) == 0u) {
-          appended = 1;
-          const uint32_t pos = atomicAdd(&a.ctrl[0], 1u);
-          if (pos < static_cast<uint32_t>(a.M))
-            __hip_atomic_store(&a.ovf_rows[pos], row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tot > C) appended = overflow_append(a, row);
       }
     }
   } else {
     __syncthreads();  // (1)
   }
 
-  // Finalize as in the large kernel: waves that appended release their list
-  // entries; the last workgroup publishes n_ovf and clears the control block.
-  if (__ballot(appended) != 0) __threadfence();
-  raw_barrier();
-  if (tid == 0) {
-    const uint32_t done = atomicAdd(&a.ctrl[1], 1u);
-    *s_last = (done == static_cast<uint32_t>(gridDim.x) - 1u);
-  }
-  waitcnt<63, 0>();
-  raw_barrier();
-  if (*s_last) {
-    __threadfence();
-    uint32_t n = __hip_atomic_load(&a.ctrl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    n = min(n, static_cast<uint32_t>(a.M));
-    for (uint32_t i = tid; i < n; i += blockDim.x) {
-      const int rr = __hip_atomic_load(&a.ovf_rows[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (rr >= 0 && rr < a.M) __hip_atomic_store(&flags[rr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == 0) {
-      *a.n_ovf = static_cast<int32_t>(n);
-      __hip_atomic_store(&a.ctrl[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  overflow_finalize(a, appended, s_last);
 }
 
 template <int RB>

@@ -12,7 +12,6 @@ using twell::align256;
 namespace {
 
 constexpr int64_t kMaxM = int64_t(1) << 30;
-constexpr int64_t kSlicedMinM = 16;  // smaller batches use the fused up/down kernel
 constexpr int64_t kMaxF = int64_t(1) << 24;
 
 struct Layout {
@@ -296,7 +295,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   // The sliced form needs two launches and 8 waves per row; below a few rows
   // the single fused launch is quicker (measured: 12.8 vs 17.2 us at M = 1,
   // d = 2048, F = 8192; equal at M = 16).
-  if (M >= kSlicedMinM && twell::sliced_supports(d, F))
+  if (M >= twell::kFewRows && twell::sliced_supports(d, F))
     st = sliced_impl(x, WuT, Wd, &p, M, d, F, T, C, at<uint8_t>(workspace, L.part), y, s);
   else
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);

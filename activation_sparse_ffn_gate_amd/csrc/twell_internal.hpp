@@ -7,9 +7,10 @@
 
 namespace twell {
 
-// Control block of the gate kernel's overflow set: ctrl[0] = entries appended
-// this call, ctrl[1] = workgroups finished, then one dedup flag per row, then
-// kDenseCounters arrival counters of the split-K fallback. Zero between calls.
+// Control block of the gate kernel's overflow set: one 64-bit word whose low
+// half (ctrl[0]) counts rows appended this call and high half (ctrl[1])
+// workgroups finished, then one dedup flag per row, then kDenseCounters
+// arrival counters of the split-K fallback. Zero between calls.
 constexpr size_t kCtrlBytes = 256;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -93,6 +94,7 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 // d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
 bool sliced_supports(int64_t d, int64_t F);
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
+constexpr int kFewRows = 256;  // below: the fused form with a workgroup per token, also in the forward
 hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);

@@ -143,6 +143,40 @@ def latency(fn, n, flush=None):
             "n": n}
 
 
+def graph_time(fn, out, calls=10, replays=20, checks=3):
+    """Milliseconds per call of `fn` replayed from a HIP graph that holds
+    `calls` back-to-back calls, so host-side launch costs drop out (they
+    dominate below ~50 us). `out` is the tensor the call writes, or None when
+    `fn` returns its result. Every checked replay must give the eager result's
+    bits, with eager work and a synchronisation between replays."""
+    import torch
+
+    r = fn()
+    torch.cuda.synchronize()
+    ref = (out if out is not None else r).clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            r = fn()
+    res = out if out is not None else r
+    same = True
+    for _ in range(checks):
+        res.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same &= bool(torch.equal(res, ref))
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    e.synchronize()
+    del g
+    return s.elapsed_time(e) / (calls * replays), same
+
+
 def dense_torch(x, Wg, WuT, Wd):
     """The dense gated FFN on hipBLASLt through torch (bf16 products, bf16
     hidden): z|u = x [Wg; WuT]^T in one GEMM, h = ReLU(z) * u, y = h Wd."""
@@ -159,8 +193,9 @@ def dense_torch(x, Wg, WuT, Wd):
     return run
 
 
-def layer_sweep(dev, names, steps, warmup):
-    """Sparse forward vs the dense baselines on each named layer."""
+def layer_sweep(dev, names, steps, warmup, graphs=False):
+    """Sparse forward vs the dense baselines on each named layer; with
+    `graphs`, every leg is timed by HIP graph replay (graph_time)."""
     import numpy as np
     import torch
 
@@ -179,12 +214,15 @@ def layer_sweep(dev, names, steps, warmup):
         fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)  # noqa: E731
         dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y, workspace=wsd)  # noqa: E731
         dt = dense_torch(x, Wg, WuT, Wd)
-        res = {}
-        for key, fn in (("sparse", fwd), ("dense", dense), ("dense_hipblaslt", dt)):
+        res, replay_ok = {}, {}
+        for key, fn, o in (("sparse", fwd, y), ("dense", dense, y), ("dense_hipblaslt", dt, None)):
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
-            res[key] = time_loop(fn, steps, stream)
+            if graphs:
+                res[key], replay_ok[key] = graph_time(fn, o, replays=max(2, steps // 10))
+            else:
+                res[key] = time_loop(fn, steps, stream)
         view = tw.packed_view(w.M, w.d, w.F, w.T, w.C, workspace=ws, device=dev)
         counts = view.counts.cpu().numpy().view(np.uint16).astype(np.int64)
         out.append({
@@ -197,6 +235,9 @@ def layer_sweep(dev, names, steps, warmup):
             "speedup_vs_dense": round(res["dense"] / res["sparse"], 3),
             "speedup_vs_dense_hipblaslt": round(res["dense_hipblaslt"] / res["sparse"], 3),
         })
+        if graphs:
+            out[-1]["timing"] = "hip_graph"
+            out[-1]["graph_replays_match_eager"] = replay_ok
         del x, Wg, WuT, Wd, y, ws, ctrl, wsd, dt, view
         torch.cuda.empty_cache()
     return out
@@ -403,7 +444,7 @@ def main():
         sweep = sorted((k for k in _W if k.startswith("sweep_")), key=lambda k: _W[k].mean_nnz)
         out["density_sweep"] = layer_sweep(dev, sweep, args.sweep_steps, 2)
         decode = sorted((k for k in _W if k.startswith("decode_")), key=lambda k: _W[k].M)
-        out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4)
+        out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4, graphs=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))

@@ -141,7 +141,7 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
                          size_t ws_bytes, void* stream);
 
 /* The whole sparse forward: twell_gate_pack, then twell_sliced_updown (or
- * twell_fused_updown below 16 rows and for the d that the sliced form does not
+ * twell_fused_updown below 256 rows and for the d that the sliced form does not
  * support), then twell_dense_fallback, on one stream, with the packing kept in
  * the workspace (see twell_packed_view). y [M, d] fp32 is fully written.
  * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */

@@ -47,6 +47,14 @@ SMALL = {
     "long_rows": scaled(WORKLOADS["sweep_p11pct"], M=96, d=512, F=8192, T=64, C=64),
     # d = 2304 is not one the sliced kernels take: the forward uses the fused one
     "fused_only_d2304": scaled(WORKLOADS["ffn1p5b"], M=200, d=2304, F=1024, mean_nnz=12.0),
+    # Few rows: the gate's 32-token tiles and the fused kernel's workgroup per
+    # token. d = 768 takes 8-byte lanes and leaves 5 of 8 waves without output
+    # columns; d = 2560 gives two column groups per lane, the second held by 2
+    # waves; 30% density at C = T = 64 never overflows and gives > 1024 list
+    # entries per 64-tile group (several LDS rounds).
+    "few_rows_d768": scaled(WORKLOADS["ffn1p5b"], M=5, d=768, F=2048),
+    "few_rows_d2560": scaled(WORKLOADS["ffn2b_zipf"], M=7, d=2560, F=2560),
+    "few_rows_dense30": scaled(WORKLOADS["sweep_p11pct"], M=9, d=512, F=8192, T=64, C=64, mean_nnz=2458.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
@@ -121,8 +129,8 @@ def test_components_compose(name):
     p = tw.gate_pack(x, Wg, w.T, w.C)
     g = host_packing(p)
     assert np.array_equal(view["counts"], g["counts"]) and np.array_equal(view["ovf"], g["ovf"])
-    # the forward's choice: the sliced form from 16 rows on, where d allows it
-    updown = tw.sliced_updown if (w.M >= 16 and sliced_ok(w.d)) else tw.fused_updown
+    # the forward's choice: the sliced form from 256 rows on, where d allows it
+    updown = tw.sliced_updown if (w.M >= 256 and sliced_ok(w.d)) else tw.fused_updown
     y = updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
     yh = y.cpu().numpy()
     ovf = g["ovf"]
@@ -153,6 +161,57 @@ def test_updown_kernels_match_definition(name):
     if "sliced" in outs:
         a, b = outs["fused"], outs["sliced"]
         assert np.abs(a - b).max() <= 1e-5 * max(np.abs(a).max(), 1e-30)
+
+
+@pytest.mark.parametrize("name", ["uniform_ragged", "zipf_small", "long_rows", "fused_only_d2304", "few_rows_d2560"])
+def test_fused_forms_agree(name):
+    """The fused kernel runs a workgroup per token below 256 rows and a wave
+    per token from 256 on; rows are independent and both forms take every
+    product and sum in the same order, so a batch's first rows alone give the
+    same bits as the whole batch. The case's rows are repeated up to 300."""
+    inp, _, _, _ = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    big = x.repeat(-(-300 // w.M), 1)[:max(300, w.M)].contiguous()
+    p = tw.gate_pack(big, Wg, w.T, w.C)
+    full = tw.fused_updown(big, WuT, Wd, p, y=nan_y(big.shape[0], w.d))
+    k = 37
+    head = tw.Packed(p.vals[:k], p.idx[:k], p.counts[:k], p.ovf_rows[:k], p.n_ovf, p.T, p.C)
+    part = tw.fused_updown(big[:k].contiguous(), WuT, Wd, head, y=nan_y(k, w.d))
+    a, b = full[:k].cpu().numpy(), part.cpu().numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))  # overflow rows: written by neither
+    assert np.isfinite(a).any()
+    assert np.array_equal(a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["few_rows_d768", "heavytail_small", "dense11_small"])
+def test_forward_graph_replay(name):
+    """The forward holds no host synchronisation and no allocation, and its
+    control block is zero again after every call, so a HIP graph of two
+    forwards replays to the eager result's bits every time (cases with and
+    without overflow rows; eager work and a synchronisation between replays)."""
+    inp, _, _, _ = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    ws, ctrl = tw.Workspace(DEV), tw.Workspace(DEV, zeroed=True)
+    y = nan_y(w.M, w.d)
+    tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(2):
+            tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)
+    for _ in range(4):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
+    del g
+    tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)  # eager again after the replays
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", list(SMALL))
