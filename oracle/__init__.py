@@ -14,12 +14,15 @@ since the pages print no worked numeric example.
 
 from .twell_oracle import (  # noqa: F401
     TwellPacking,
+    column_activity,
     column_rms,
+    compact_rows,
     decode_bf16,
     dense_gated_ffn,
     ffn_from_active_set,
     ffn_from_twell,
     gate_preactivations,
+    live_layout,
     overflow_rows,
     pack_twell,
     unpack_twell,

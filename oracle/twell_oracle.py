@@ -212,3 +212,44 @@ def column_rms(Z: np.ndarray) -> np.ndarray:
     """Root-mean-square of each column of Z over all rows (tokens)."""
     Z = np.asarray(Z, dtype=np.float64)
     return np.sqrt(np.mean(Z * Z, axis=0))
+
+
+# ------------------------------------------------------------- dead gate units
+# [pulsen], dead-neuron paragraph: at the recommended L1 coefficient more than
+# 30% of the gate units end up never active; [tencent] section 6: too strong a
+# regularisation leaves such dead neurons. The pages re-initialise them during
+# training. At inference the plain consequence is taken: a unit that no token
+# activates contributes exact zeros to every output row, so its rows can be
+# dropped from Wg, WuT and Wd without changing y, and the gate product shrinks.
+
+
+def column_activity(Z: np.ndarray) -> np.ndarray:
+    """Units active for at least one token: any over rows of Z[r, j] > 0.
+
+    Same strict activity test as the packing (+0, -0 and NaN are inactive).
+    """
+    return np.asarray(np.asarray(Z) > 0).any(axis=0)
+
+
+def live_layout(active: np.ndarray, T: int) -> np.ndarray:
+    """Source column of each column of the compacted layer.
+
+    The active columns in ascending order, then -1 (a zero row, never active:
+    its pre-activation is exactly 0) up to the next multiple of T, so the
+    compacted width stays whole TwELL tiles; at least one tile.
+    """
+    live = np.flatnonzero(np.asarray(active, dtype=bool))
+    width = max(T, -(-len(live) // T) * T)
+    src = np.full(width, -1, dtype=np.int64)
+    src[: len(live)] = live
+    return src
+
+
+def compact_rows(W: np.ndarray, src: np.ndarray) -> np.ndarray:
+    """Rows W[src[i]] (bf16 bits), and a zero row where src[i] < 0."""
+    W = np.asarray(W)
+    out = np.zeros((len(src),) + W.shape[1:], dtype=W.dtype)
+    for i, s in enumerate(np.asarray(src)):
+        if s >= 0:
+            out[i] = W[s]
+    return out

@@ -22,6 +22,13 @@ What pins what:
   ffn_from_active_set    equal to the dense definition (skipped terms are exact
                          zeros), including rows that overflow.
 * column_rms             a closed-form 2x2 case.
+* column_activity,
+  live_layout,
+  compact_rows           hand-worked cases (strict activity, ascending order,
+                         padding to whole tiles, zero padding rows); and on
+                         random layers with planted dead units, the dense
+                         definition on the compacted weights equals it on the
+                         full weights (dropped terms are exact zeros).
 """
 
 import types
@@ -299,10 +306,56 @@ def pin_column_rms(o):
     assert np.allclose(got, [np.sqrt(4.5), np.sqrt(8.0)], rtol=0, atol=1e-15)
 
 
+def pin_column_activity(o):
+    Z = np.array([[0.0, -1.0, 2.0, -0.0, np.nan, 1e-40],
+                  [0.0, -3.0, -2.0, -5.0, -np.inf, -1e-40],
+                  [-1.0, -2.0, 0.0, 0.0, np.nan, 0.0]])
+    assert o.column_activity(Z).tolist() == [False, False, True, False, False, True]
+    assert o.column_activity(np.zeros((0, 3))).tolist() == [False, False, False]
+
+
+def pin_live_layout(o):
+    act = np.array([False, True, False, True, True, False, False, False, True])
+    assert o.live_layout(act, 4).tolist() == [1, 3, 4, 8]
+    assert o.live_layout(act, 3).tolist() == [1, 3, 4, 8, -1, -1]
+    assert o.live_layout(np.zeros(8, dtype=bool), 4).tolist() == [-1, -1, -1, -1]
+    assert o.live_layout(np.ones(8, dtype=bool), 4).tolist() == list(range(8))
+
+
+def pin_compact_rows(o):
+    W = np.arange(12, dtype=np.uint16).reshape(4, 3)
+    got = o.compact_rows(W, np.array([2, 0, -1]))
+    assert got.dtype == np.uint16
+    assert got.tolist() == [[6, 7, 8], [0, 1, 2], [0, 0, 0]]
+
+
+def pin_compaction_keeps_ffn(o):
+    rng = np.random.default_rng(7)
+    M, d, F, T = 9, 8, 24, 4
+    x = rand_bf16(rng, (M, d))
+    x[:, 0] = bf([1.0])[0]
+    Wg, WuT, Wd = (rand_bf16(rng, (F, d), 0.5) for _ in range(3))
+    dead = rng.permutation(F)[:10]
+    Wg[dead, 0] = bf([-64.0])[0]  # z = -64 + (bounded rest) < 0 for every token
+    Z = o.gate_preactivations(x, Wg)
+    act = o.column_activity(Z)
+    assert not act[dead].any() and act.sum() >= 4
+    src = o.live_layout(act, T)
+    Wg_c, WuT_c, Wd_c = (o.compact_rows(W, src) for W in (Wg, WuT, Wd))
+    y = o.dense_gated_ffn(x, Wg, WuT, Wd)
+    y_c = o.dense_gated_ffn(x, Wg_c, WuT_c, Wd_c)
+    assert np.abs(y_c - y).max() <= 1e-12 * max(np.abs(y).max(), 1e-300)
+    # dropping one live unit does change y: the equality above is not vacuous
+    src_short = src[src >= 0][1:]
+    y_s = o.dense_gated_ffn(x, *(o.compact_rows(W, src_short) for W in (Wg, WuT, Wd)))
+    assert np.abs(y_s - y).max() > 1e-6 * np.abs(y).max()
+
+
 PINS = [
     pin_decode, pin_hand_example, pin_integer_bruteforce, pin_relu_identity, pin_all_active,
     pin_zero_density, pin_pack_csr, pin_pack_rowwise_ell, pin_pack_strict, pin_overflow_boundary,
     pin_sparse_equals_dense, pin_unpack_roundtrip, pin_column_rms,
+    pin_column_activity, pin_live_layout, pin_compact_rows, pin_compaction_keeps_ffn,
 ]
 
 
@@ -429,6 +482,13 @@ MUTANTS = {
     "unpack_no_tile_offset": dict(unpack_twell=_unpack_no_tile_offset),
     "active_set_negative": dict(ffn_from_active_set=lambda x, WuT, Wd, Z: O.ffn_from_active_set(x, WuT, Wd, -Z)),
     "rms_no_sqrt": dict(column_rms=lambda Z: np.mean(np.asarray(Z) ** 2, axis=0)),
+    "activity_ge": dict(column_activity=lambda Z: (np.asarray(Z) >= 0).any(axis=0)),
+    "activity_all_rows": dict(column_activity=lambda Z: (np.asarray(Z) > 0).all(axis=0)),
+    "layout_no_padding": dict(live_layout=lambda a, T: np.flatnonzero(a)),
+    "layout_descending": dict(live_layout=lambda a, T: O.live_layout(a, T)[::-1].copy()),
+    "layout_pad_with_zero_col": dict(live_layout=lambda a, T: np.maximum(O.live_layout(a, T), 0)),
+    "compact_off_by_one": dict(compact_rows=lambda W, src: O.compact_rows(W, np.where(src >= 0, (src + 1) % len(W), src))),
+    "compact_pad_copies": dict(compact_rows=lambda W, src: np.asarray(W)[np.asarray(src)]),
 }
 
 
