@@ -6,6 +6,7 @@ passes device pointers of torch tensors and the current stream, nothing more.
 """
 
 from ._lib import (  # noqa: F401
+    OP_COLUMN_ACTIVITY,
     OP_DENSE_FALLBACK,
     OP_DENSE_FFN,
     OP_FFN_FORWARD,
@@ -15,14 +16,18 @@ from ._lib import (  # noqa: F401
     Packed,
     TwellError,
     Workspace,
+    column_activity,
+    compact_layer,
     ctrl_bytes,
     dense_fallback,
     dense_ffn_forward,
     ffn_forward,
     fused_updown,
     gate_pack,
+    gather_rows,
     header_functions,
     lib,
+    live_layout,
     packed_view,
     sliced_updown,
     status_string,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libtwell.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "twell.h")
 
 TWELL_OK = 0
-OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK, OP_SLICED_UPDOWN = 0, 1, 2, 3, 4
+OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK, OP_SLICED_UPDOWN, OP_COLUMN_ACTIVITY = 0, 1, 2, 3, 4, 5
 
 
 class TwellError(RuntimeError):
@@ -46,6 +46,9 @@ _SIGNATURES = {
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "twell_column_activity": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
+    "twell_live_layout": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, ctypes.POINTER(_I64)]),
+    "twell_gather_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "twell_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32]),
     "twell_ctrl_bytes": (_SZ, [_I64]),
     "twell_packed_view": (ctypes.c_int, [_P, _SZ, _I64, _I64, _I64, _I32, _I32, _PK]),
@@ -289,6 +292,69 @@ def dense_ffn_forward(x, Wg, WuT, Wd, y=None, workspace=None):
     wp, wn = ws.get(workspace_bytes(OP_DENSE_FFN, M, d, F))
     _check(lib().twell_dense_ffn_forward(*args, M, d, F, _dptr(y), wp, wn, _stream(x)), "twell_dense_ffn_forward")
     return y
+
+
+def column_activity(x, Wg, T: int, C: int, bits=None, workspace=None, ctrl=None):
+    """twell_column_activity: ORs this batch's unit activity into `bits`
+    (int32 [ceil(F / 32)] on x's device; a zeroed one when None) and returns it."""
+    torch = _torch()
+    M, d = x.shape
+    F = Wg.shape[0]
+    px, pw = _bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d))
+    nwords = -(-F // 32)
+    if bits is None:
+        bits = torch.zeros(nwords, dtype=torch.int32, device=x.device)
+    elif bits.dtype != torch.int32 or tuple(bits.shape) != (nwords,) or not bits.is_contiguous() or not bits.is_cuda:
+        raise ValueError(f"bits must be a contiguous int32 device tensor of shape ({nwords},)")
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_COLUMN_ACTIVITY, M, d, F, T, C))
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    _check(lib().twell_column_activity(px, pw, M, d, F, T, C, _dptr(bits), cp, cn, wp, wn, _stream(x)),
+           "twell_column_activity")
+    return bits
+
+
+def live_layout(bits, F: int, T: int):
+    """twell_live_layout (host): numpy int32 source unit of each compacted unit
+    (-1 = zero row). bits: host uint32/int32 array or tensor of ceil(F / 32) words."""
+    import numpy as np
+
+    b = bits.cpu().numpy() if hasattr(bits, "cpu") else np.asarray(bits)
+    b = np.ascontiguousarray(b).view(np.uint32)
+    if b.shape != (-(-F // 32),):
+        raise ValueError(f"bits must hold {-(-F // 32)} words")
+    width = ctypes.c_int64(0)
+    _check(lib().twell_live_layout(b.ctypes.data_as(ctypes.c_void_p), F, T, None, 0, ctypes.byref(width)),
+           "twell_live_layout")
+    src = np.empty(width.value, dtype=np.int32)
+    _check(lib().twell_live_layout(b.ctypes.data_as(ctypes.c_void_p), F, T, src.ctypes.data_as(ctypes.c_void_p),
+                                   len(src), ctypes.byref(width)), "twell_live_layout")
+    return src
+
+
+def gather_rows(W, src, out=None):
+    """twell_gather_rows: out[i] = W[src[i]], a zero row for src[i] < 0.
+    src: int32 device tensor [n]."""
+    torch = _torch()
+    F, d = W.shape
+    pw = _bf16(W, "W", (F, d))
+    if src.dtype != torch.int32 or src.dim() != 1 or not src.is_contiguous() or not src.is_cuda:
+        raise ValueError("src must be a contiguous 1-D int32 device tensor")
+    n = src.shape[0]
+    if out is None:
+        out = torch.empty((n, d), dtype=W.dtype, device=W.device)
+    po = _bf16(out, "out", (n, d))
+    _check(lib().twell_gather_rows(pw, F, d, _dptr(src), n, po, _stream(W)), "twell_gather_rows")
+    return out
+
+
+def compact_layer(Wg, WuT, Wd, bits, T: int):
+    """The layer without its never-active units: (Wg_c, WuT_c, Wd_c, src),
+    src the int32 device tensor of source units (-1 = zero padding row)."""
+    torch = _torch()
+    src = torch.from_numpy(live_layout(bits, Wg.shape[0], T)).to(Wg.device)
+    return gather_rows(Wg, src), gather_rows(WuT, src), gather_rows(Wd, src), src
 
 
 def packed_view(M: int, d: int, F: int, T: int, C: int, workspace=None, device=None) -> Packed:

@@ -42,7 +42,7 @@ constexpr int kTileBytes = 256 * kBK * 2;  // one operand tile of a stage (16 KB
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kDmaPerStage = 8;  // global_load_lds per thread per stage (4 for A, 4 for B)
 
-template <int kT, bool kDebug>
+template <int kT, bool kDebug, bool kAct>
 __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m, int tiles_n) {
   // One LDS object only: with a second one the compiler attaches alias scopes
   // to LDS accesses and then makes every LDS read wait for all outstanding
@@ -238,11 +238,17 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 #pragma unroll
   for (int tt = 0; tt < kTilesPerWave; ++tt) cnt[tt][0] = cnt[tt][1] = 0;
 
+  uint64_t act[4] = {0, 0, 0, 0};  // column activity (kAct): OR of the ballots
+
   static_for<0, 64>([&](auto g) {
     constexpr int mb = decltype(g)::value / 16, v = decltype(g)::value % 16;
     uint64_t bal[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) bal[nb] = __ballot(acc[mb][nb][v] > 0.f);
+    if constexpr (kAct) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) act[nb] |= bal[nb];
+    }
     if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;  // both tokens inactive here
     constexpr int rl_lo = mb * 32 + acc_row(v, 0);  // token of lanes 0-31; lanes 32-63: +4
     constexpr int h = rl_lo >> 6, l_lo = rl_lo & 63;
@@ -283,6 +289,17 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
     }
   });
 
+  // Column activity: one OR per 32-unit block (both halves of a ballot hold
+  // the same 32 units, for two tokens), skipped past the last tile.
+  if constexpr (kAct) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t word = static_cast<uint32_t>(act[nb]) | static_cast<uint32_t>(act[nb] >> 32);
+      if (tile0 + nb / kBlocksPerTile < nT && word != 0u && lane == 0)
+        atomicOr(&a.col_active[(wcol0 >> 5) + nb], word);
+    }
+  }
+
   // Counts: lane L writes tokens wrow0 + L and wrow0 + 64 + L; overflow rows
   // join the set.
   int appended = 0;
@@ -316,13 +333,15 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.F + kBN - 1) / kBN;
   const dim3 grid(tiles_m * tiles_n), block(256);
-  const bool dbg = a.z_debug != nullptr;
+  const bool dbg = a.z_debug != nullptr, act = a.col_active != nullptr;
   if (a.T == 128) {
-    if (dbg) gate_pack_kernel<128, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
-    else gate_pack_kernel<128, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    if (dbg) gate_pack_kernel<128, true, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else if (act) gate_pack_kernel<128, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else gate_pack_kernel<128, false, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
   } else {
-    if (dbg) gate_pack_kernel<64, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
-    else gate_pack_kernel<64, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    if (dbg) gate_pack_kernel<64, true, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else if (act) gate_pack_kernel<64, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    else gate_pack_kernel<64, false, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

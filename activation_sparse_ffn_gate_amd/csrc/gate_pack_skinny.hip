@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t sk_off(int r, int p) {
   return static_cast<uint32_t>(r * kRowB + ((p ^ (r & 15)) << 4));
 }
 
-template <int kT, bool kDebug, int RB>
+template <int kT, bool kDebug, bool kAct, int RB>
 __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateArgs a, int tiles_m) {
   using S = SkinnyShape<RB>;
   constexpr int kSM = S::kSM;
@@ -210,6 +210,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
       cw = writelane<32 * b + acc_row(v, 0)>(cw, __popc(static_cast<uint32_t>(bal[b][v])));
       cw = writelane<32 * b + acc_row(v, 1)>(cw, __popc(static_cast<uint32_t>(bal[b][v] >> 32)));
     });
+    if constexpr (kAct) {  // column activity of the wave's 32 units
+      uint64_t any = 0;
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) any |= bal[b][v];
+      const uint32_t word = static_cast<uint32_t>(any) | static_cast<uint32_t>(any >> 32);
+      if (word != 0u && lane == 0) atomicOr(&a.col_active[(n0 + wn * 32) >> 5], word);
+    }
     if (lane < kSM) s_cnt[wn][lane] = cw;
     __syncthreads();  // (1) counts of every wave
     // Lane t: active units of token t in the tile's lower waves, and in all of them.
@@ -260,13 +269,15 @@ hipError_t launch_rb(const GateArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + 32 * RB - 1) / (32 * RB);
   const int tiles_n = (a.F + kSN - 1) / kSN;
   const dim3 grid(tiles_m * tiles_n), block(64 * kWaves);
-  const bool dbg = a.z_debug != nullptr;
+  const bool dbg = a.z_debug != nullptr, act = a.col_active != nullptr;
   if (a.T == 128) {
-    if (dbg) gate_pack_skinny_kernel<128, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_skinny_kernel<128, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_skinny_kernel<128, true, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else if (act) gate_pack_skinny_kernel<128, false, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<128, false, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
   } else {
-    if (dbg) gate_pack_skinny_kernel<64, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
-    else gate_pack_skinny_kernel<64, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    if (dbg) gate_pack_skinny_kernel<64, true, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else if (act) gate_pack_skinny_kernel<64, false, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
+    else gate_pack_skinny_kernel<64, false, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
   }
   return hipGetLastError();
 }

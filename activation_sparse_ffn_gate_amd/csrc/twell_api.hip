@@ -41,6 +41,13 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
   switch (op) {
     case TWELL_OP_GATE_PACK:
       break;
+    case TWELL_OP_COLUMN_ACTIVITY:  // a packing that is thrown away
+      L.vals = take(m * nT * size_t(C) * 4);
+      L.idx = take(m * nT * size_t(C));
+      L.counts = take(m * nT * 2);
+      L.ovf_rows = take(m * 4);
+      L.n_ovf = take(4);
+      break;
     case TWELL_OP_FFN_FORWARD: {
       L.vals = take(m * nT * size_t(C) * 4);
       L.idx = take(m * nT * size_t(C));
@@ -129,7 +136,7 @@ twell_packed packed_in_ws(void* ws, const Layout& L) {
 
 int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F, int32_t T,
                    int32_t C, const twell_packed* out, float* z_debug, uint32_t* ctrl,
-                   hipStream_t s) {
+                   hipStream_t s, uint32_t* col_active = nullptr) {
   if (M == 0) return hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
   twell::GateArgs a;
   a.x = x;
@@ -146,6 +153,7 @@ int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, 
   a.n_ovf = out->n_ovf;
   a.ctrl = ctrl;
   a.z_debug = z_debug;
+  a.col_active = col_active;
   return hip_status(twell::launch_gate_pack(a, s));
 }
 
@@ -318,9 +326,53 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
                     nullptr, y, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
+int twell_column_activity(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
+                          int32_t T, int32_t C, uint32_t* active_bits, void* ctrl, size_t ctrl_bytes_,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  if ((M != 0 && !x) || !Wg || !active_bits) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_COLUMN_ACTIVITY, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  if (M == 0) return TWELL_OK;
+  const twell_packed p = packed_in_ws(workspace, layout(TWELL_OP_COLUMN_ACTIVITY, M, F, T, C));
+  return gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl),
+                        static_cast<hipStream_t>(stream), active_bits);
+}
+
+int twell_live_layout(const uint32_t* active_bits, int64_t F, int32_t T, int32_t* src, int64_t cap,
+                      int64_t* width) {
+  if (!active_bits || !width || F <= 0 || F > kMaxF || T < 1) return TWELL_E_INVALID_ARG;
+  int64_t live = 0;
+  for (int64_t j = 0; j < F; ++j) live += (active_bits[j >> 5] >> (j & 31)) & 1u;
+  const int64_t w = std::max<int64_t>(T, (live + T - 1) / T * T);
+  *width = w;
+  if (src == nullptr) return TWELL_OK;
+  if (cap < w) return TWELL_E_INVALID_ARG;
+  int64_t i = 0;
+  for (int64_t j = 0; j < F; ++j)
+    if ((active_bits[j >> 5] >> (j & 31)) & 1u) src[i++] = static_cast<int32_t>(j);
+  for (; i < w; ++i) src[i] = -1;
+  return TWELL_OK;
+}
+
+int twell_gather_rows(const uint16_t* W, int64_t F, int64_t d, const int32_t* src, int64_t n,
+                      uint16_t* out, void* stream) {
+  if (n < 0) return TWELL_E_INVALID_ARG;
+  if (n == 0) return TWELL_OK;
+  if (!W || !src || !out) return TWELL_E_INVALID_ARG;
+  int st = check_dims(1, d, F);
+  if (st != TWELL_OK) return st;
+  if (n > kMaxF) return TWELL_E_INVALID_ARG;
+  return hip_status(twell::launch_gather_rows(W, int(F), int(d), src, int(n), out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
   if (check_dims(M, d, F) != TWELL_OK) return 0;
-  if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD || op == TWELL_OP_SLICED_UPDOWN) {
+  if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD || op == TWELL_OP_SLICED_UPDOWN ||
+      op == TWELL_OP_COLUMN_ACTIVITY) {
     if (check_tc(F, T, C) != TWELL_OK) return 0;
     if (op == TWELL_OP_SLICED_UPDOWN && !twell::sliced_supports(d, F)) return 0;
   } else if (op == TWELL_OP_DENSE_FFN || op == TWELL_OP_DENSE_FALLBACK) {

@@ -26,6 +26,7 @@ struct GateArgs {
   int32_t* n_ovf;
   uint32_t* ctrl;   // kCtrlBytes, then flags[M]
   float* z_debug;   // nullable
+  uint32_t* col_active;  // nullable: bit j % 32 of word j / 32 ORed with "some row has z_j > 0"
 };
 
 struct FusedArgs {
@@ -95,6 +96,10 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 bool sliced_supports(int64_t d, int64_t F);
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
 constexpr int kFewRows = 256;  // below: the fused form with a workgroup per token, also in the forward
+// Row gather: out[i] = W[src[i]] for 0 <= src[i] < F, else a zero row.
+hipError_t launch_gather_rows(const uint16_t* W, int F, int d, const int32_t* src, int n, uint16_t* out,
+                              hipStream_t s);
+
 hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);

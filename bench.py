@@ -18,6 +18,7 @@ sparse/dense ratio at every point.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -101,6 +102,8 @@ def parse():
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc outputs under DIR (no GPU needed)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the density sweep")
+    ap.add_argument("--compact", action="store_true",
+                    help="with --only: run on the layer with its never-active units dropped")
     ap.add_argument("--sweep-steps", type=int, default=10)
     return ap.parse_args()
 
@@ -243,6 +246,59 @@ def layer_sweep(dev, names, steps, warmup, graphs=False):
     return out
 
 
+def dead_unit_compaction(dev, name, steps, warmup):
+    """The layer with its never-active units dropped (activity taken over the
+    layer's own batch), against the full layer: forward and gate times, the
+    compacted width, and how far the two outputs are apart."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    x, Wg, WuT, Wd = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+                      for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+    stream = torch.cuda.current_stream(dev)
+    bits = tw.column_activity(x, Wg, w.T, w.C)
+    t0 = time.perf_counter()
+    Wg_c, WuT_c, Wd_c, src = tw.compact_layer(Wg, WuT, Wd, bits, w.T)
+    torch.cuda.synchronize()
+    t_compact = time.perf_counter() - t0
+    Fc = Wg_c.shape[0]
+    live = int((src >= 0).sum().item())
+    y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
+    y_c = torch.empty_like(y)
+    ws, ws_c = tw.Workspace(dev), tw.Workspace(dev)
+    p, p_c = tw.Packed.empty(w.M, w.F, w.T, w.C, dev), tw.Packed.empty(w.M, Fc, w.T, w.C, dev)
+    legs = {
+        "forward": lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws),
+        "forward_compacted": lambda: tw.ffn_forward(x, Wg_c, WuT_c, Wd_c, w.T, w.C, y=y_c, workspace=ws_c),
+        "gate": lambda: tw.gate_pack(x, Wg, w.T, w.C, out=p),
+        "gate_compacted": lambda: tw.gate_pack(x, Wg_c, w.T, w.C, out=p_c),
+    }
+    res = {}
+    for key, fn in legs.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        res[key] = time_loop(fn, steps, stream)
+    legs["forward"]()
+    legs["forward_compacted"]()
+    torch.cuda.synchronize()
+    diff = float((y_c - y).norm() / y.norm())
+    out = {"workload": name, "F": w.F, "live_units": live, "F_compacted": Fc,
+           "dead_units_by_construction": int(inp.info["dead"].sum()) if "dead" in inp.info else None,
+           "compaction_s": round(t_compact, 4), "rel_l2_full_vs_compacted": diff}
+    out.update({f"{k}_ms": round(v, 5) for k, v in res.items()})
+    out["forward_speedup"] = round(res["forward"] / res["forward_compacted"], 3)
+    out["gate_speedup"] = round(res["gate"] / res["gate_compacted"], 3)
+    del x, Wg, WuT, Wd, Wg_c, WuT_c, Wd_c, y, y_c, ws, ws_c, p, p_c
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle, as it stands, on a bounded sample of the same layer's rows."""
     import numpy as np
@@ -298,6 +354,14 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     x, Wg, WuT, Wd = (td(a) for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+    if args.compact:  # the layer without its never-active units (activity over its own batch)
+        if args.only is None:
+            print("--compact is for --only runs (the default run reports it in dead_unit_compaction)",
+                  file=sys.stderr)
+            return 2
+        bits = tw.column_activity(x, Wg, w.T, w.C)
+        Wg, WuT, Wd, _ = tw.compact_layer(Wg, WuT, Wd, bits, w.T)
+        w = dataclasses.replace(w, F=Wg.shape[0])
     y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     ws_fwd = tw.Workspace(dev)
@@ -445,6 +509,7 @@ def main():
         out["density_sweep"] = layer_sweep(dev, sweep, args.sweep_steps, 2)
         decode = sorted((k for k in _W if k.startswith("decode_")), key=lambda k: _W[k].M)
         out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4, graphs=True)
+        out["dead_unit_compaction"] = dead_unit_compaction(dev, "ffn1p5b_heavytail", 2 * args.sweep_steps, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 2
+#define TWELL_ABI_VERSION 3
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -65,6 +65,7 @@ extern "C" {
 #define TWELL_OP_DENSE_FFN 2
 #define TWELL_OP_DENSE_FALLBACK 3
 #define TWELL_OP_SLICED_UPDOWN 4
+#define TWELL_OP_COLUMN_ACTIVITY 5
 
 /* TwELL packing of ReLU(x Wg^T) with tile width T and capacity C
  * (the format: tgviewer.app Telegram post, part "Вот тут и решает TwELL";
@@ -157,6 +158,43 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Dead gate units (pulsen.vercel.app article, dead-neuron paragraph: at the
+ * recommended L1 coefficient over 30% of the units are never active; Tencent
+ * Cloud article, section 6). A unit that no token activates adds exact zeros
+ * to every output row, so dropping its rows from Wg, WuT and Wd leaves y
+ * unchanged for inputs that keep it inactive, and shrinks the gate product.
+ * The three calls below find such units over calibration batches and build
+ * the compacted layer; twell_ffn_forward then runs on it unchanged (F = the
+ * compacted width). */
+
+/* Gate GEMM of x with the activity of every unit recorded: bit (j % 32) of
+ * active_bits[j / 32] is ORed with 1 when z_j = x_r . Wg_j > 0 for some row r
+ * (the packing's activity test, in the same fp32 arithmetic). active_bits:
+ * device [ceil(F / 32)] uint32, zeroed by the caller before the first batch;
+ * calls accumulate, so several batches give the union. ctrl: >=
+ * twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_COLUMN_ACTIVITY,
+ * ...), holds a packing that is discarded. */
+int twell_column_activity(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
+                          int32_t T, int32_t C, uint32_t* active_bits, void* ctrl, size_t ctrl_bytes,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* HOST function (no GPU work): the compacted layout from activity bits. The
+ * active units in ascending order, then -1 (a zero row) up to the next
+ * multiple of T; at least T entries. active_bits: host [ceil(F / 32)] as
+ * written by twell_column_activity; T >= 1. *width receives the compacted
+ * width; src: host [cap] int32 receives the source unit of each compacted
+ * unit, or NULL to query the width only. TWELL_E_INVALID_ARG when cap <
+ * width (nothing is written to src then). */
+int twell_live_layout(const uint32_t* active_bits, int64_t F, int32_t T, int32_t* src, int64_t cap,
+                      int64_t* width);
+
+/* out[i] = W[src[i]] for i < n, a zero row where src[i] < 0 or src[i] >= F.
+ * W: device [F, d] bf16; src: device [n] int32; out: device [n, d] bf16, not
+ * overlapping W. d as for the other calls. One call per weight matrix builds
+ * the compacted Wg, WuT and Wd from one src. */
+int twell_gather_rows(const uint16_t* W, int64_t F, int64_t d, const int32_t* src, int64_t n,
+                      uint16_t* out, void* stream);
 
 /* Workspace bytes an operation needs (0 for invalid arguments). T and C are
  * ignored for TWELL_OP_DENSE_FFN and TWELL_OP_DENSE_FALLBACK;

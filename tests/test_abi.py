@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 2
+    assert L.twell_abi_version() == 3
     for s in (OK, E_ARG, E_UNSUP, E_WS, -4):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"
@@ -145,3 +145,62 @@ def test_packed_view_is_host_arithmetic():
     nT = F // T
     assert pk.idx - pk.vals >= M * nT * C * 4 and pk.counts - pk.idx >= M * nT * C
     assert L.twell_packed_view(ctypes.c_void_p(base), ws - 1, M, d, F, T, C, ctypes.byref(pk)) == E_WS
+
+
+# ------------------------------------------------------------- dead gate units
+@pytest.mark.parametrize("F,T,density,seed", [(1024, 64, 0.7, 1), (8192, 128, 0.7, 2), (192, 64, 0.0, 3),
+                                              (256, 128, 1.0, 4), (4096, 128, 0.01, 5), (96, 7, 0.5, 6)])
+def test_live_layout_matches_oracle(F, T, density, seed):
+    """twell_live_layout is host code: checked against the oracle's layout."""
+    import numpy as np
+
+    import oracle as O
+
+    rng = np.random.default_rng(seed)
+    active = rng.random(F) < density
+    words = np.zeros(-(-F // 32), dtype=np.uint32)
+    for j in np.flatnonzero(active):
+        words[j // 32] |= np.uint32(1 << (j % 32))
+    got = tw.live_layout(words, F, T)
+    want = O.live_layout(active, T)
+    assert got.dtype == np.int32 and np.array_equal(got.astype(np.int64), want)
+
+
+def test_live_layout_validation():
+    import numpy as np
+
+    L = tw.lib()
+    words = np.full(2, 0xFFFFFFFF, dtype=np.uint32)
+    pw = words.ctypes.data_as(ctypes.c_void_p)
+    width = ctypes.c_int64(-1)
+    assert L.twell_live_layout(pw, 64, 64, None, 0, ctypes.byref(width)) == OK and width.value == 64
+    assert L.twell_live_layout(pw, 60, 64, None, 0, ctypes.byref(width)) == OK and width.value == 64
+    src = np.full(8, 7, dtype=np.int32)
+    assert L.twell_live_layout(pw, 64, 64, src.ctypes.data_as(ctypes.c_void_p), 8, ctypes.byref(width)) == E_ARG
+    assert (src == 7).all()  # nothing written when src is too short
+    assert L.twell_live_layout(None, 64, 64, None, 0, ctypes.byref(width)) == E_ARG
+    assert L.twell_live_layout(pw, 0, 64, None, 0, ctypes.byref(width)) == E_ARG
+    assert L.twell_live_layout(pw, 64, 0, None, 0, ctypes.byref(width)) == E_ARG
+    assert L.twell_live_layout(pw, 64, 64, None, 0, None) == E_ARG
+
+
+def test_column_activity_and_gather_validation():
+    L = tw.lib()
+    M, d, F, T, C = 64, 256, 1024, 64, 8
+    ws = tw.workspace_bytes(tw.OP_COLUMN_ACTIVITY, M, d, F, T, C)
+    nT = F // T
+    assert ws >= M * nT * C * 5 + M * nT * 2 + 4 * M
+    g = tw.ctrl_bytes(M)
+    ok = (FAKE, FAKE, M, d, F, T, C, FAKE, FAKE, g, FAKE, ws, None)
+    f = L.twell_column_activity
+    assert f(*ok[:7], None, *ok[8:]) == E_ARG  # no activity bits
+    assert f(FAKE, FAKE, M, d, F, T, C, FAKE, FAKE, g, FAKE, ws - 256, None) == E_WS
+    assert f(FAKE, FAKE, M, d, F, T, C, FAKE, FAKE, g - 256, FAKE, ws, None) == E_WS
+    assert f(FAKE, FAKE, M, d, F, 96, C, FAKE, FAKE, g, FAKE, ws, None) == E_UNSUP
+    assert f(FAKE, FAKE, M, 320, F, T, C, FAKE, FAKE, g, FAKE, ws, None) == E_UNSUP
+    gr = L.twell_gather_rows
+    assert gr(FAKE, F, d, FAKE, -1, FAKE, None) == E_ARG
+    assert gr(None, F, d, None, 0, None, None) == OK  # nothing to do
+    assert gr(None, F, d, FAKE, 4, FAKE, None) == E_ARG
+    assert gr(FAKE, F, 100, FAKE, 4, FAKE, None) == E_UNSUP
+    assert gr(FAKE, 0, d, FAKE, 4, FAKE, None) == E_ARG

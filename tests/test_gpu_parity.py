@@ -214,6 +214,61 @@ def test_forward_graph_replay(name):
     assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
 
 
+def _bits_to_mask(bits, F):
+    w = bits.cpu().numpy().view(np.uint32)
+    return ((w[np.arange(F) // 32] >> (np.arange(F) % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+@pytest.mark.parametrize("name", ["heavytail_small", "uniform_ragged", "t64_odd_tiles", "few_rows_d768",
+                                  "dense11_small", "zipf_small"])
+def test_column_activity(name):
+    """Unit activity over the batch: equal to the oracle's on the kernel's own
+    z (bit-exact mode); against fp64 z only near-zero columns may differ;
+    never-active units by construction stay inactive; two half batches
+    accumulate to the whole batch's bits."""
+    inp, Z, rms, _ = small_case(name)
+    w = inp.workload
+    x, Wg, _, _ = dev(inp)
+    bits = tw.column_activity(x, Wg, w.T, w.C)
+    got = _bits_to_mask(bits, w.F)
+    _, z32 = run_gate(inp, debug=True)
+    assert np.array_equal(got, O.column_activity(z32))
+    ref = O.column_activity(Z)
+    diff = np.flatnonzero(got != ref)
+    for j in diff:  # a differing column may only hold |z| near zero where the two disagree
+        rows = np.flatnonzero((z32[:, j] > 0) != (Z[:, j] > 0))
+        assert np.abs(Z[rows, j]).max() < 1e-3 * rms[j]
+    if "dead" in inp.info and inp.info["dead"].any():
+        assert not got[inp.info["dead"]].any()
+    k = w.M // 2
+    acc = tw.column_activity(x[:k].contiguous(), Wg, w.T, w.C)
+    acc = tw.column_activity(x[k:].contiguous(), Wg, w.T, w.C, bits=acc)
+    assert torch.equal(acc, bits)
+
+
+@pytest.mark.parametrize("name", ["heavytail_small", "t64_odd_tiles", "few_rows_d2560"])
+def test_compacted_layer(name):
+    """The layer without its never-active units: rows bit-exact against the
+    oracle's selection, and the forward on it equals the full layer's
+    definition (the dropped units contribute exact zeros)."""
+    inp, Z, _, Y = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    bits = tw.column_activity(x, Wg, w.T, w.C)
+    Wg_c, WuT_c, Wd_c, src = tw.compact_layer(Wg, WuT, Wd, bits, w.T)
+    _, z32 = run_gate(inp, debug=True)
+    want_src = O.live_layout(O.column_activity(z32), w.T)
+    assert np.array_equal(src.cpu().numpy().astype(np.int64), want_src)
+    for dev_c, host in ((Wg_c, inp.Wg), (WuT_c, inp.WuT), (Wd_c, inp.Wd)):
+        got = dev_c.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, O.compact_rows(host, want_src))
+    Fc = Wg_c.shape[0]
+    assert Fc % w.T == 0 and Fc <= w.F
+    y = tw.ffn_forward(x, Wg_c, WuT_c, Wd_c, w.T, w.C, y=nan_y(w.M, w.d)).cpu().numpy()
+    rel, mx = check_y(y, Y)
+    print(f"{name}: F {w.F} -> {Fc} live+pad, rel L2 {rel:.2e}")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_dense_baseline(name):
     inp, _, _, Y = small_case(name)
