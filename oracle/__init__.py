@@ -13,6 +13,7 @@ since the pages print no worked numeric example.
 """
 
 from .twell_oracle import (  # noqa: F401
+    HybridFormat,
     TwellPacking,
     column_activity,
     column_rms,
@@ -20,8 +21,11 @@ from .twell_oracle import (  # noqa: F401
     decode_bf16,
     dense_gated_ffn,
     ffn_from_active_set,
+    ffn_backward,
+    ffn_backward_from_hybrid,
     ffn_from_twell,
     gate_preactivations,
+    hybrid_pack,
     live_layout,
     overflow_rows,
     pack_twell,

@@ -253,3 +253,115 @@ def compact_rows(W: np.ndarray, src: np.ndarray) -> np.ndarray:
         if s >= 0:
             out[i] = W[s]
     return out
+
+
+# ------------------------------------------------- training: hybrid format, backward
+# [tgviewer] part "Обучение" and [tencent] section 3: for training every row of
+# the gate output is either compressed into one sparse block whose width is the
+# same for all rows ("globally aligned"), or, when it holds too many active
+# units, kept as a dense row in a reserve; with it the backward pass needs no
+# product of two dense matrices. Readings: the sparse block holds the row's
+# active units (z > 0, the packing's test) in ascending column order with their
+# gate values g = ReLU(z), width K for every row; a row with more than K active
+# units goes to the reserve whole, as its dense g row.
+
+
+@dataclass
+class HybridFormat:
+    idx: np.ndarray  # [M, K] int64 global unit of slot s (-1 past the count or for reserve rows)
+    vals: np.ndarray  # [M, K] float32 g of that unit (0 where idx is -1)
+    count: np.ndarray  # [M] int64 active units of the row (any size; > K for reserve rows)
+    res_rows: np.ndarray  # [R] int64 rows held densely, ascending
+    res_vals: np.ndarray  # [R, F] float32 their dense g rows
+
+
+def hybrid_pack(Z: np.ndarray, K: int) -> HybridFormat:
+    """Rows of ReLU(Z) (fp32 bits kept) in the hybrid training format."""
+    Z = np.asarray(Z, dtype=np.float32)
+    M, F = Z.shape
+    idx = np.full((M, K), -1, dtype=np.int64)
+    vals = np.zeros((M, K), dtype=np.float32)
+    count = np.zeros(M, dtype=np.int64)
+    res = []
+    for r in range(M):
+        cols = [j for j in range(F) if Z[r, j] > 0]
+        count[r] = len(cols)
+        if len(cols) > K:
+            res.append(r)
+            continue
+        for s, j in enumerate(cols):
+            idx[r, s] = j
+            vals[r, s] = Z[r, j]
+    res_rows = np.array(res, dtype=np.int64)
+    res_vals = np.where(Z[res_rows] > 0, Z[res_rows], np.float32(0)).astype(np.float32)
+    return HybridFormat(idx, vals, count, res_rows, res_vals.reshape(len(res_rows), F))
+
+
+def _ffn_forward_f64(X, Wg, WuT, Wd):
+    Z = X @ Wg.T
+    G = np.maximum(Z, 0.0)
+    U = X @ WuT.T
+    return Z, G, U, (G * U) @ Wd
+
+
+def _ffn_backward_f64(X, Wg, WuT, Wd, dY):
+    """Gradients of y = (ReLU(x Wg^T) ⊙ x WuT^T) Wd by the chain rule, fp64:
+    dH = dY Wd^T, dZ = dH ⊙ U ⊙ [Z > 0], dU = dH ⊙ G,
+    dX = dZ Wg + dU WuT, dWg = dZ^T X, dWuT = dU^T X, dWd = H^T dY
+    (ReLU'(0) taken as 0, matching the strict activity test)."""
+    Z, G, U, _ = _ffn_forward_f64(X, Wg, WuT, Wd)
+    dH = dY @ Wd.T
+    dZ = dH * U * (Z > 0)
+    dU = dH * G
+    return dZ @ Wg + dU @ WuT, dZ.T @ X, dU.T @ X, (G * U).T @ dY
+
+
+def _f64(a):
+    """bf16 bits (uint16) decoded exactly; floating arrays taken as they are."""
+    a = np.asarray(a)
+    return decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def ffn_backward(x, Wg, WuT, Wd, dy):
+    """(dx, dWg, dWuT, dWd) of the gated FFN for upstream gradient dy, fp64,
+    from bf16 bits (dy too) or from floating arrays. Dense definition; dWuT
+    is the gradient of WuT (row j = unit j), matching the weights' [F, d]
+    layout."""
+    return _ffn_backward_f64(*(_f64(a) for a in (x, Wg, WuT, Wd, dy)))
+
+
+def ffn_backward_from_hybrid(hy: HybridFormat, x, Wg, WuT, Wd, dy):
+    """The same gradients evaluated only on the active units listed by the
+    hybrid format (sparse rows) and the reserve rows' dense g rows, fp64.
+
+    Every term left out has g = 0 and z <= 0, so its dZ, dU and H are exact
+    zeros; this is the definition itself, summed over the non-zero terms.
+    """
+    X, Wg_, WuT_, Wd_, dY = (_f64(a) for a in (x, Wg, WuT, Wd, dy))
+    M, d = X.shape
+    F = Wg_.shape[0]
+    dX = np.zeros((M, d))
+    dWg = np.zeros((F, d))
+    dWu = np.zeros((F, d))
+    dWd = np.zeros((F, d))
+    res = {int(r): i for i, r in enumerate(hy.res_rows)}
+    for r in range(M):
+        if r in res:
+            g_row = hy.res_vals[res[r]].astype(np.float64)
+            units = np.flatnonzero(g_row > 0)
+            g = g_row[units]
+        else:
+            n = int(hy.count[r])
+            units = hy.idx[r, :n]
+            g = hy.vals[r, :n].astype(np.float64)
+        if len(units) == 0:
+            continue
+        u = WuT_[units] @ X[r]
+        dh = Wd_[units] @ dY[r]
+        dz = dh * u
+        du = dh * g
+        dX[r] = dz @ Wg_[units] + du @ WuT_[units]
+        dWg[units] += np.outer(dz, X[r])
+        dWu[units] += np.outer(du, X[r])
+        dWd[units] += np.outer(g * u, dY[r])
+    return dX, dWg, dWu, dWd

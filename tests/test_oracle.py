@@ -22,6 +22,14 @@ What pins what:
   ffn_from_active_set    equal to the dense definition (skipped terms are exact
                          zeros), including rows that overflow.
 * column_rms             a closed-form 2x2 case.
+* ffn_backward           a hand-worked example with closed-form gradients;
+                         central finite differences of <y, dy> along random
+                         directions, for x and all three weights (fp64 inputs,
+                         no pre-activation near the ReLU kink).
+* hybrid_pack            a hand-worked example (ascending order, width K,
+                         reserve rows kept whole as dense g rows).
+* ffn_backward_from_hybrid  equal to the dense definition, reserve rows
+                         included.
 * column_activity,
   live_layout,
   compact_rows           hand-worked cases (strict activity, ascending order,
@@ -351,11 +359,79 @@ def pin_compaction_keeps_ffn(o):
     assert np.abs(y_s - y).max() > 1e-6 * np.abs(y).max()
 
 
+def pin_backward_hand_example(o):
+    # x = [1, 2]; z = [1, -2]; g = [1, 0]; u = [3, 2]; h = [3, 0]; dy = [1, 1]
+    # dH = [1, 1]; dZ = [3, 0]; dU = [1, 0]; dx = 3 [1, 0] + 1 [1, 1] = [4, 1]
+    x = bf([[1.0, 2.0]])
+    Wg = bf([[1.0, 0.0], [0.0, -1.0]])
+    WuT = bf([[1.0, 1.0], [2.0, 0.0]])
+    Wd = bf([[1.0, 0.0], [0.0, 1.0]])
+    dy = bf([[1.0, 1.0]])
+    dx, dWg, dWu, dWd = o.ffn_backward(x, Wg, WuT, Wd, dy)
+    assert dx.tolist() == [[4.0, 1.0]]
+    assert dWg.tolist() == [[3.0, 6.0], [0.0, 0.0]]
+    assert dWu.tolist() == [[1.0, 2.0], [0.0, 0.0]]
+    assert dWd.tolist() == [[3.0, 3.0], [0.0, 0.0]]
+
+
+def pin_backward_finite_difference(o):
+    rng = np.random.default_rng(11)
+    M, d, F = 5, 6, 7
+    P = [rng.standard_normal(s) for s in ((M, d), (F, d), (F, d), (F, d))]
+    Z = P[0] @ P[1].T
+    P[1][np.abs(Z).min(axis=0) < 0.05] *= -1.0  # keep clear of the kink (re-checked below)
+    assert np.abs(P[0] @ P[1].T).min() > 1e-3
+    R = rng.standard_normal((M, d))
+
+    def loss(X, Wg, WuT, Wd):  # <y, R> with y written out from its definition
+        return float(np.sum(((np.maximum(X @ Wg.T, 0) * (X @ WuT.T)) @ Wd) * R))
+
+    grads = o.ffn_backward(*P, R)
+    eps = 1e-6
+    for i in range(4):
+        V = rng.standard_normal(P[i].shape)
+        hi = [p + eps * V if k == i else p for k, p in enumerate(P)]
+        lo = [p - eps * V if k == i else p for k, p in enumerate(P)]
+        fd = (loss(*hi) - loss(*lo)) / (2 * eps)
+        an = float(np.sum(grads[i] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (i, fd, an)
+
+
+def pin_hybrid_pack(o):
+    Z = np.array([[0.5, -1.0, 2.0, 0.0, 3.0],
+                  [-1.0, -2.0, -3.0, -4.0, -5.0],
+                  [1.0, 2.0, 3.0, -1.0, 4.0],
+                  [0.0, 0.0, 7.0, 0.0, 0.0]], dtype=np.float32)
+    h = o.hybrid_pack(Z, 3)
+    assert h.count.tolist() == [3, 0, 4, 1]
+    assert h.idx.tolist() == [[0, 2, 4], [-1, -1, -1], [-1, -1, -1], [2, -1, -1]]
+    assert h.vals.tolist() == [[0.5, 2.0, 3.0], [0, 0, 0], [0, 0, 0], [7.0, 0, 0]]
+    assert h.res_rows.tolist() == [2]
+    assert h.res_vals.tolist() == [[1.0, 2.0, 3.0, 0.0, 4.0]]
+
+
+def pin_backward_hybrid_equals_dense(o):
+    rng = np.random.default_rng(12)
+    M, d, F, K = 7, 16, 24, 12
+    x = rand_bf16(rng, (M, d))
+    Wg, WuT, Wd = (rand_bf16(rng, (F, d), 0.5) for _ in range(3))
+    dy = rand_bf16(rng, (M, d))
+    Z = o.gate_preactivations(x, Wg)
+    h = o.hybrid_pack(Z.astype(np.float32), K)
+    assert len(h.res_rows) >= 1 and (h.count <= K).sum() >= 1  # both kinds of rows occur
+    want = o.ffn_backward(x, Wg, WuT, Wd, dy)
+    got = o.ffn_backward_from_hybrid(h, x, Wg, WuT, Wd, dy)
+    for a, b in zip(got, want):  # g went through fp32 in the format
+        assert np.abs(a - b).max() <= 1e-6 * max(np.abs(b).max(), 1e-300)
+
+
 PINS = [
     pin_decode, pin_hand_example, pin_integer_bruteforce, pin_relu_identity, pin_all_active,
     pin_zero_density, pin_pack_csr, pin_pack_rowwise_ell, pin_pack_strict, pin_overflow_boundary,
     pin_sparse_equals_dense, pin_unpack_roundtrip, pin_column_rms,
     pin_column_activity, pin_live_layout, pin_compact_rows, pin_compaction_keeps_ffn,
+    pin_backward_hand_example, pin_backward_finite_difference, pin_hybrid_pack,
+    pin_backward_hybrid_equals_dense,
 ]
 
 
@@ -489,7 +565,46 @@ MUTANTS = {
     "layout_pad_with_zero_col": dict(live_layout=lambda a, T: np.maximum(O.live_layout(a, T), 0)),
     "compact_off_by_one": dict(compact_rows=lambda W, src: O.compact_rows(W, np.where(src >= 0, (src + 1) % len(W), src))),
     "compact_pad_copies": dict(compact_rows=lambda W, src: np.asarray(W)[np.asarray(src)]),
+    "bwd_no_relu_mask": dict(ffn_backward=lambda *a: _bwd_variant("no_mask", *a)),
+    "bwd_du_uses_u": dict(ffn_backward=lambda *a: _bwd_variant("du_u", *a)),
+    "bwd_dx_drops_du": dict(ffn_backward=lambda *a: _bwd_variant("dx_no_du", *a)),
+    "bwd_dwd_uses_g": dict(ffn_backward=lambda *a: _bwd_variant("dwd_g", *a)),
+    "bwd_dwg_uses_du": dict(ffn_backward=lambda *a: _bwd_variant("dwg_du", *a)),
+    "hybrid_ge_k": dict(hybrid_pack=lambda Z, K: _hybrid_variant("ge", Z, K)),
+    "hybrid_descending": dict(hybrid_pack=lambda Z, K: _hybrid_variant("desc", Z, K)),
+    "hybrid_reserve_z": dict(hybrid_pack=lambda Z, K: _hybrid_variant("res_z", Z, K)),
+    "hybrid_bwd_drops_reserve": dict(ffn_backward_from_hybrid=lambda h, *a: O.ffn_backward_from_hybrid(
+        O.HybridFormat(h.idx, h.vals, h.count, h.res_rows[:0], h.res_vals[:0]), *a)),
 }
+
+
+def _bwd_variant(kind, x, Wg, WuT, Wd, dy):
+    X, G_, U_, D_, dY = (O._f64(a) for a in (x, Wg, WuT, Wd, dy))
+    Z = X @ G_.T
+    G = np.maximum(Z, 0)
+    U = X @ U_.T
+    dH = dY @ D_.T
+    dZ = dH * U * (1.0 if kind == "no_mask" else (Z > 0))
+    dU = dH * (U if kind == "du_u" else G)
+    dX = dZ @ G_ + (0 if kind == "dx_no_du" else dU @ U_)
+    dWg = (dU if kind == "dwg_du" else dZ).T @ X
+    dWd = (G if kind == "dwd_g" else G * U).T @ dY
+    return dX, dWg, dU.T @ X, dWd
+
+
+def _hybrid_variant(kind, Z, K):
+    h = O.hybrid_pack(Z, K - 1 if kind == "ge" else K)
+    if kind == "ge":
+        return O.HybridFormat(np.pad(h.idx, ((0, 0), (0, 1)), constant_values=-1),
+                              np.pad(h.vals, ((0, 0), (0, 1))), h.count, h.res_rows, h.res_vals)
+    if kind == "desc":
+        idx, vals = h.idx.copy(), h.vals.copy()
+        for r in range(len(idx)):
+            n = int(min(h.count[r], K)) if r not in set(h.res_rows.tolist()) else 0
+            idx[r, :n], vals[r, :n] = idx[r, :n][::-1], vals[r, :n][::-1]
+        return O.HybridFormat(idx, vals, h.count, h.res_rows, h.res_vals)
+    Zr = np.asarray(Z, dtype=np.float32)[h.res_rows]
+    return O.HybridFormat(h.idx, h.vals, h.count, h.res_rows, Zr)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
