@@ -13,19 +13,23 @@ from ._lib import (  # noqa: F401
     OP_GATE_PACK,
     OP_SLICED_UPDOWN,
     LIB_PATH,
+    Hybrid,
     Packed,
     TwellError,
     Workspace,
     column_activity,
     compact_layer,
+    backward_workspace_bytes,
     ctrl_bytes,
     dense_fallback,
     dense_ffn_forward,
+    ffn_backward,
     ffn_forward,
     fused_updown,
     gate_pack,
     gather_rows,
     header_functions,
+    hybrid_pack,
     lib,
     live_layout,
     packed_view,

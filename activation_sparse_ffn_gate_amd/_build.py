@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["gate_pack.hip", "gate_pack_skinny.hip", "fused_updown.hip", "sliced_updown.hip", "dense_ffn.hip",
-           "compact_rows.hip",
+           "compact_rows.hip", "backward.hip",
            "twell_api.hip"]
 
 # Packed fp32 VALU ops are turned off for every device compile.

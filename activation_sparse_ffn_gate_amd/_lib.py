@@ -37,8 +37,20 @@ class _Packed(ctypes.Structure):
     ]
 
 
+class _Hybrid(ctypes.Structure):
+    _fields_ = [
+        ("idx", ctypes.c_void_p),
+        ("vals", ctypes.c_void_p),
+        ("count", ctypes.c_void_p),
+        ("res_rows", ctypes.c_void_p),
+        ("res_vals", ctypes.c_void_p),
+        ("n_res", ctypes.c_void_p),
+    ]
+
+
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _PK = ctypes.POINTER(_Packed)
+_PH = ctypes.POINTER(_Hybrid)
 _SIGNATURES = {
     "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
     "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
@@ -49,6 +61,10 @@ _SIGNATURES = {
     "twell_column_activity": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_live_layout": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, ctypes.POINTER(_I64)]),
     "twell_gather_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "twell_hybrid_pack": (ctypes.c_int, [_PK, _I64, _I64, _I32, _I32, _I32, _I64, _PH, _P]),
+    "twell_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32, _I64]),
+    "twell_ffn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _PH, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P,
+                                          _P, _SZ, _P]),
     "twell_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32]),
     "twell_ctrl_bytes": (_SZ, [_I64]),
     "twell_packed_view": (ctypes.c_int, [_P, _SZ, _I64, _I64, _I64, _I32, _I32, _PK]),
@@ -355,6 +371,73 @@ def compact_layer(Wg, WuT, Wd, bits, T: int):
     torch = _torch()
     src = torch.from_numpy(live_layout(bits, Wg.shape[0], T)).to(Wg.device)
     return gather_rows(Wg, src), gather_rows(WuT, src), gather_rows(Wd, src), src
+
+
+@dataclass
+class Hybrid:
+    """Device tensors of the hybrid training format (see twell_hybrid in include/twell.h)."""
+
+    idx: "object"  # int32 [M, K]
+    vals: "object"  # float32 [M, K]
+    count: "object"  # int32 [M]
+    res_rows: "object"  # int32 [R]
+    res_vals: "object"  # float32 [R, F]
+    n_res: "object"  # int32 [1]
+    K: int
+    R: int
+
+    @classmethod
+    def empty(cls, M, F, K, R, device):
+        torch = _torch()
+        return cls(
+            torch.empty((M, K), dtype=torch.int32, device=device),
+            torch.empty((M, K), dtype=torch.float32, device=device),
+            torch.empty((M,), dtype=torch.int32, device=device),
+            torch.empty((R,), dtype=torch.int32, device=device),
+            torch.empty((R, F), dtype=torch.float32, device=device),
+            torch.empty((1,), dtype=torch.int32, device=device),
+            K,
+            R,
+        )
+
+    def _c(self) -> _Hybrid:
+        return _Hybrid(*(_dptr(t).value or 0 for t in (self.idx, self.vals, self.count, self.res_rows,
+                                                        self.res_vals, self.n_res)))
+
+
+def hybrid_pack(packed: Packed, F: int, K: int, R: int, out: Hybrid | None = None) -> Hybrid:
+    """twell_hybrid_pack: the hybrid format from a packing with C == T."""
+    M = packed.counts.shape[0]
+    out = out or Hybrid.empty(M, F, K, R, packed.counts.device)
+    pk, ph = packed._c(), out._c()
+    _check(lib().twell_hybrid_pack(ctypes.byref(pk), M, F, packed.T, packed.C, K, R, ctypes.byref(ph),
+                                   _stream(packed.counts)), "twell_hybrid_pack")
+    return out
+
+
+def backward_workspace_bytes(M: int, d: int, F: int, K: int, R: int) -> int:
+    return int(lib().twell_backward_workspace_bytes(M, d, F, K, R))
+
+
+def ffn_backward(x, Wg, WuT, Wd, dy, hy: Hybrid, workspace=None, out=None):
+    """twell_ffn_backward: (dx, dWg, dWuT, dWd), fp32. out: optional tuple of
+    the four output tensors to overwrite."""
+    torch = _torch()
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)),
+            _bf16(dy, "dy", (M, d)))
+    if out is None:
+        out = (torch.empty((M, d), dtype=torch.float32, device=x.device),
+               *(torch.empty((F, d), dtype=torch.float32, device=x.device) for _ in range(3)))
+    shapes = ((M, d), (F, d), (F, d), (F, d))
+    ptrs = [_dptr(_f32_out(t, n, sh, x.device)) for t, n, sh in zip(out, ("dx", "dWg", "dWuT", "dWd"), shapes)]
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(backward_workspace_bytes(M, d, F, hy.K, hy.R))
+    ph = hy._c()
+    _check(lib().twell_ffn_backward(*args, ctypes.byref(ph), M, d, F, hy.K, hy.R, *ptrs, wp, wn, _stream(x)),
+           "twell_ffn_backward")
+    return out
 
 
 def packed_view(M: int, d: int, F: int, T: int, C: int, workspace=None, device=None) -> Packed:

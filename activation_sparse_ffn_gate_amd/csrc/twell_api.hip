@@ -225,9 +225,133 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   return hip_status(twell::launch_dense(a, s));
 }
 
+// Workspace of twell_ffn_backward: row offsets, the entry list (keys, two
+// permutations, sorted keys, rows, h, dz, du) and the sort's scratch.
+struct BwdLayout {
+  size_t row_off = 0, keys = 0, perm_in = 0, keys_sorted = 0, perm = 0, e_row = 0, e_h = 0, e_dz = 0, e_du = 0;
+  size_t sort = 0, sort_bytes = 0, total = 0;
+  int64_t E_max = 0;
+};
+
+int check_bwd(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
+  if (M < 0 || d <= 0 || F <= 0 || K < 1 || R < 0 || R > M) return TWELL_E_INVALID_ARG;
+  if (M > kMaxM || F > kMaxF) return TWELL_E_INVALID_ARG;
+  if (!twell::backward_supports_d(int(d))) return TWELL_E_UNSUPPORTED;
+  if (M * int64_t(K) + R * F >= (int64_t(1) << 31)) return TWELL_E_UNSUPPORTED;
+  return TWELL_OK;
+}
+
+BwdLayout bwd_layout(int64_t M, int64_t F, int32_t K, int64_t R) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.E_max = M * int64_t(K) + R * F;
+  const size_t e4 = size_t(L.E_max) * 4;
+  L.row_off = take(size_t(M + 1) * 4);
+  L.keys = take(e4);
+  L.perm_in = take(e4);
+  L.keys_sorted = take(e4);
+  L.perm = take(e4);
+  L.e_row = take(e4);
+  L.e_h = take(e4);
+  L.e_dz = take(e4);
+  L.e_du = take(e4);
+  L.sort_bytes = twell::backward_sort_bytes(L.E_max, int(F));
+  L.sort = take(std::max<size_t>(L.sort_bytes, 1));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+int twell_hybrid_pack(const twell_packed* in, int64_t M, int64_t F, int32_t T, int32_t C, int32_t K,
+                      int64_t R, const twell_hybrid* out, void* stream) {
+  if (!in || !out || !out->n_res) return TWELL_E_INVALID_ARG;
+  if (M < 0 || M > kMaxM || F <= 0 || F > kMaxF || K < 1 || R < 0 || R > M) return TWELL_E_INVALID_ARG;
+  int st = check_tc(F, T, C);
+  if (st != TWELL_OK) return st;
+  if (C != T) return TWELL_E_UNSUPPORTED;  // the packing must hold every active unit
+  if (M != 0 && (!in->vals || !in->idx || !in->counts || !out->idx || !out->vals || !out->count))
+    return TWELL_E_INVALID_ARG;
+  if (R != 0 && (!out->res_rows || !out->res_vals)) return TWELL_E_INVALID_ARG;
+  twell::HybridArgs a;
+  a.vals = in->vals;
+  a.idx = in->idx;
+  a.counts = in->counts;
+  a.M = int(M);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.K = K;
+  a.R = int(R);
+  a.h_idx = out->idx;
+  a.h_vals = out->vals;
+  a.h_count = out->count;
+  a.res_rows = out->res_rows;
+  a.res_vals = out->res_vals;
+  a.n_res = out->n_res;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) return hip_status(twell::launch_set_i32(out->n_res, 0, s));
+  return hip_status(twell::launch_hybrid_pack(a, s));
+}
+
+size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
+  if (check_bwd(M, d, F, K, R) != TWELL_OK) return 0;
+  return bwd_layout(M, F, K, R).total;
+}
+
+int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                       const uint16_t* dy, const twell_hybrid* hy, int64_t M, int64_t d, int64_t F,
+                       int32_t K, int64_t R, float* dx, float* dWg, float* dWuT, float* dWd,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!Wg || !WuT || !Wd || !hy || !hy->n_res || !dWg || !dWuT || !dWd) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!x || !dy || !dx || !hy->idx || !hy->vals || !hy->count)) return TWELL_E_INVALID_ARG;
+  if (R != 0 && !hy->res_vals) return TWELL_E_INVALID_ARG;
+  int st = check_bwd(M, d, F, K, R);
+  if (st != TWELL_OK) return st;
+  const BwdLayout L = bwd_layout(M, F, K, R);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || ws_bytes < L.total)
+    return TWELL_E_WORKSPACE;
+  twell::BackwardArgs a;
+  a.x = x;
+  a.Wg = Wg;
+  a.WuT = WuT;
+  a.Wd = Wd;
+  a.dy = dy;
+  a.h_idx = hy->idx;
+  a.h_vals = hy->vals;
+  a.h_count = hy->count;
+  a.res_vals = hy->res_vals;
+  a.n_res = hy->n_res;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.K = K;
+  a.R = int(R);
+  a.E_max = L.E_max;
+  a.dx = dx;
+  a.dWg = dWg;
+  a.dWu = dWuT;
+  a.dWd = dWd;
+  a.row_off = at<int32_t>(workspace, L.row_off);
+  a.keys = at<int32_t>(workspace, L.keys);
+  a.perm_in = at<int32_t>(workspace, L.perm_in);
+  a.keys_sorted = at<int32_t>(workspace, L.keys_sorted);
+  a.perm = at<int32_t>(workspace, L.perm);
+  a.e_row = at<int32_t>(workspace, L.e_row);
+  a.e_h = at<float>(workspace, L.e_h);
+  a.e_dz = at<float>(workspace, L.e_dz);
+  a.e_du = at<float>(workspace, L.e_du);
+  a.sort_tmp = at<uint8_t>(workspace, L.sort);
+  a.sort_bytes = L.sort_bytes;
+  return hip_status(twell::launch_backward(a, static_cast<hipStream_t>(stream)));
+}
 
 int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
                     int32_t T, int32_t C, const twell_packed* out, float* z_debug, void* ctrl,

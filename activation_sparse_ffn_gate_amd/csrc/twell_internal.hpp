@@ -96,6 +96,42 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 bool sliced_supports(int64_t d, int64_t F);
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
 constexpr int kFewRows = 256;  // below: the fused form with a workgroup per token, also in the forward
+// Hybrid training format from a complete TwELL packing (C == T).
+struct HybridArgs {
+  const float* vals;
+  const uint8_t* idx;
+  const uint16_t* counts;
+  int M, F, T, C, K, R;
+  int32_t* h_idx;     // [M, K] global units, ascending; a reserve row's slot 0 holds its reserve slot
+  float* h_vals;      // [M, K]
+  int32_t* h_count;   // [M]
+  int32_t* res_rows;  // [R]
+  float* res_vals;    // [R, F]
+  int32_t* n_res;     // [1]
+};
+hipError_t launch_hybrid_pack(const HybridArgs& a, hipStream_t s);
+
+// Sparse backward over the hybrid format; entry list and sort buffers in a workspace.
+struct BackwardArgs {
+  const uint16_t *x, *Wg, *WuT, *Wd, *dy;
+  const int32_t* h_idx;
+  const float* h_vals;
+  const int32_t* h_count;
+  const float* res_vals;
+  const int32_t* n_res;
+  int M, d, F, K, R;
+  int64_t E_max;  // entry capacity: M K + R F
+  float *dx, *dWg, *dWu, *dWd;
+  int32_t* row_off;  // [M + 1]
+  int32_t *keys, *perm_in, *keys_sorted, *perm, *e_row;  // [E_max]
+  float *e_h, *e_dz, *e_du;                               // [E_max]
+  void* sort_tmp;
+  size_t sort_bytes;
+};
+bool backward_supports_d(int d);
+size_t backward_sort_bytes(int64_t n, int F);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
+
 // Row gather: out[i] = W[src[i]] for 0 <= src[i] < F, else a zero row.
 hipError_t launch_gather_rows(const uint16_t* W, int F, int d, const int32_t* src, int n, uint16_t* out,
                               hipStream_t s);

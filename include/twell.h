@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 3
+#define TWELL_ABI_VERSION 4
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -195,6 +195,50 @@ int twell_live_layout(const uint32_t* active_bits, int64_t F, int32_t T, int32_t
  * the compacted Wg, WuT and Wd from one src. */
 int twell_gather_rows(const uint16_t* W, int64_t F, int64_t d, const int32_t* src, int64_t n,
                       uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------ training
+ * Hybrid training format (tgviewer.app Telegram post, part "Обучение";
+ * Tencent Cloud article, section 3): each row of ReLU(x Wg^T) is either one
+ * sparse block of width K (the same for every row) holding the row's active
+ * units, or, with more than K active units, a dense row in a reserve of R
+ * rows. With it the backward pass below multiplies no two dense matrices.
+ *   idx      [M, K] int32 global unit of slot s, ascending, s < count; for a
+ *                   reserve row slot 0 holds its reserve slot instead
+ *   vals     [M, K] fp32  g = ReLU(z) of that unit
+ *   count    [M]    int32 active units of the row (> K: the row is in the reserve)
+ *   res_rows [R]    int32 rows held densely, order unspecified, first *n_res valid
+ *   res_vals [R, F] fp32  their dense g rows
+ *   n_res    [1]    int32 rows that needed the reserve; when it exceeds R the
+ *                   reserve is incomplete and a backward over it is not valid */
+typedef struct twell_hybrid {
+  int32_t* idx;
+  float* vals;
+  int32_t* count;
+  int32_t* res_rows;
+  float* res_vals;
+  int32_t* n_res;
+} twell_hybrid;
+
+/* The hybrid format from a TwELL packing that holds every active unit:
+ * C must equal T (then no tile count exceeds C). K >= 1; 0 <= R <= M. */
+int twell_hybrid_pack(const twell_packed* in, int64_t M, int64_t F, int32_t T, int32_t C, int32_t K,
+                      int64_t R, const twell_hybrid* out, void* stream);
+
+/* Workspace bytes of twell_ffn_backward (0 for invalid arguments). */
+size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R);
+
+/* Gradients of y = (ReLU(x Wg^T) ⊙ x WuT^T) Wd for upstream gradient dy
+ * (bf16 [M, d]), over the hybrid format `hy` of this x (twell_hybrid_pack):
+ * dx [M, d], dWg, dWuT, dWd [F, d], all fp32 and overwritten. Only active
+ * units enter (their dZ, dU and h are the only non-zeros): per token, row
+ * gathers of WuT, Wd and Wg; per unit, gathers of the x and dy rows of its
+ * tokens in token order. Sums have a fixed order (deterministic).
+ * d: multiples of 512 up to 8192, or odd multiples of 256 below 4096.
+ * M K + R F < 2^31. workspace >= twell_backward_workspace_bytes(...). */
+int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                       const uint16_t* dy, const twell_hybrid* hy, int64_t M, int64_t d, int64_t F,
+                       int32_t K, int64_t R, float* dx, float* dWg, float* dWuT, float* dWd,
+                       void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs (0 for invalid arguments). T and C are
  * ignored for TWELL_OP_DENSE_FFN and TWELL_OP_DENSE_FALLBACK;

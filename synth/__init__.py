@@ -11,6 +11,7 @@ from .inputs import (  # noqa: F401
     Inputs,
     Workload,
     make_inputs,
+    make_upstream_grad,
     scaled,
     sweep_workloads,
 )

@@ -294,3 +294,16 @@ def make_inputs(w: Workload, seed: int | None = None) -> Inputs:
     # realised counts come from the data and are measured by the consumers.
     info.update(token_scale=a, n_target=n_target, dead=dead, saturated=saturated, theta=theta)
     return Inputs(w, x, Wg, WuT, Wd, info)
+
+
+# --------------------------------------------------------- training side
+_DY = 8  # a ninth stream of the same SeedSequence: the first eight are unchanged
+
+
+def make_upstream_grad(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Upstream gradient dy for the backward: bf16 bits [M, d], N(0, 1/d)
+    (the scale of a loss gradient spread over d outputs), RNE-rounded."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(_DY + 1)[_DY])
+    dy = rng.standard_normal((w.M, w.d), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.d))
+    return _to_bf16_bits(dy)

@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 3
+    assert L.twell_abi_version() == 4
     for s in (OK, E_ARG, E_UNSUP, E_WS, -4):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"
@@ -204,3 +204,32 @@ def test_column_activity_and_gather_validation():
     assert gr(None, F, d, FAKE, 4, FAKE, None) == E_ARG
     assert gr(FAKE, F, 100, FAKE, 4, FAKE, None) == E_UNSUP
     assert gr(FAKE, 0, d, FAKE, 4, FAKE, None) == E_ARG
+
+
+# ------------------------------------------------------------ training side
+def test_backward_validation():
+    from activation_sparse_ffn_gate_amd._lib import _Hybrid
+
+    L = tw.lib()
+    M, d, F, T, K, R = 64, 256, 1024, 64, 8, 4
+    ws = tw.backward_workspace_bytes(M, d, F, K, R)
+    assert ws >= 8 * 4 * (M * K + R * F)
+    assert tw.backward_workspace_bytes(M, 320, F, K, R) == 0      # d not supported
+    assert tw.backward_workspace_bytes(M, d, F, 0, R) == 0        # K >= 1
+    assert tw.backward_workspace_bytes(M, d, F, K, M + 1) == 0    # R <= M
+    assert tw.backward_workspace_bytes(1 << 24, d, F, 256, 0) == 0  # entry list past 2^31
+    pk = _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    hy = _Hybrid(*([FAKE.value] * 6))
+    hp = L.twell_hybrid_pack
+    assert hp(ctypes.byref(pk), M, F, T, 8, K, R, ctypes.byref(hy), None) == E_UNSUP  # C != T drops units
+    assert hp(ctypes.byref(pk), M, F, T, T, 0, R, ctypes.byref(hy), None) == E_ARG
+    assert hp(ctypes.byref(pk), M, F, T, T, K, M + 1, ctypes.byref(hy), None) == E_ARG
+    assert hp(None, M, F, T, T, K, R, ctypes.byref(hy), None) == E_ARG
+    fb = L.twell_ffn_backward
+    ok = [FAKE] * 5 + [ctypes.byref(hy), M, d, F, K, R] + [FAKE] * 4
+    assert fb(*ok, FAKE, ws - 256, None) == E_WS
+    assert fb(*ok, ctypes.c_void_p(FAKE.value + 8), ws, None) == E_WS  # misaligned
+    bad_d = ok[:7] + [320] + ok[8:]
+    assert fb(*bad_d, FAKE, ws, None) == E_UNSUP
+    no_dx = ok[:11] + [None] + ok[12:]
+    assert fb(*no_dx, FAKE, ws, None) == E_ARG

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from synth import WORKLOADS, make_inputs, scaled
+from synth import WORKLOADS, make_inputs, make_upstream_grad, scaled
 
 from _parity import (
     check_active_set,
@@ -267,6 +267,78 @@ def test_compacted_layer(name):
     y = tw.ffn_forward(x, Wg_c, WuT_c, Wd_c, w.T, w.C, y=nan_y(w.M, w.d)).cpu().numpy()
     rel, mx = check_y(y, Y)
     print(f"{name}: F {w.F} -> {Fc} live+pad, rel L2 {rel:.2e}")
+
+
+# ------------------------------------------------------------------ training
+# (case, K, R): K near the mean active count so both kinds of rows occur; the
+# reserve holds every row that needs it.
+TRAIN = {
+    "tiny": (48, 64),
+    "uniform_ragged": (8, 300),
+    "heavytail_small": (40, 1100),
+    "zipf_small": (16, 520),
+    "few_rows_d768": (6, 5),
+}
+
+
+@functools.lru_cache(maxsize=1)
+def train_case(name):
+    inp = make_inputs(SMALL[name] if name in SMALL else WORKLOADS[name])
+    w = inp.workload
+    K, R = TRAIN[name]
+    x, Wg, WuT, Wd = dev(inp)
+    z = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV)
+    p = tw.gate_pack(x, Wg, w.T, w.T, z_debug=z)  # C = T: every active unit is kept
+    hy = tw.hybrid_pack(p, w.F, K, R)
+    torch.cuda.synchronize()
+    z32 = z.cpu().numpy()
+    return inp, z32, O.hybrid_pack(z32, K), hy, make_upstream_grad(w)
+
+
+@pytest.mark.parametrize("name", list(TRAIN))
+def test_hybrid_pack(name):
+    """Hybrid format against the oracle's on the kernel's own z: bit-exact."""
+    inp, z32, ref, hy, _ = train_case(name)
+    w = inp.workload
+    K, R = TRAIN[name]
+    count = hy.count.cpu().numpy()
+    assert np.array_equal(count, ref.count)
+    idx, vals = hy.idx.cpu().numpy(), hy.vals.cpu().numpy()
+    for r in np.flatnonzero(count <= K):
+        n = count[r]
+        assert np.array_equal(idx[r, :n], ref.idx[r, :n])
+        assert np.array_equal(vals[r, :n].view(np.uint32), ref.vals[r, :n].view(np.uint32))
+    n_res = int(hy.n_res.item())
+    assert n_res == len(ref.res_rows) and n_res <= R
+    rows = hy.res_rows.cpu().numpy()[:n_res]
+    assert np.array_equal(np.sort(rows), ref.res_rows)
+    dense = hy.res_vals.cpu().numpy()[:n_res]
+    order = np.argsort(rows)
+    assert np.array_equal(dense[order].view(np.uint32), ref.res_vals.view(np.uint32))
+    for i, r in enumerate(rows):  # a reserve row's block names its slot
+        assert idx[r, 0] == i
+    print(f"{name}: K={K}, reserve rows {n_res} of {w.M}, mean count {count.mean():.1f}")
+
+
+@pytest.mark.parametrize("name", list(TRAIN))
+def test_backward(name):
+    """dx, dWg, dWuT, dWd against the oracle on the same active set (fp64
+    sparse evaluation of the oracle's hybrid format) and against the dense
+    definition; two runs give the same bits."""
+    inp, z32, ref, hy, dy_bits = train_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    dy = to_device(dy_bits, DEV)
+    got = [t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, dy, hy)]
+    want = O.ffn_backward_from_hybrid(ref, inp.x, inp.Wg, inp.WuT, inp.Wd, dy_bits)
+    dense = O.ffn_backward(inp.x, inp.Wg, inp.WuT, inp.Wd, dy_bits)
+    for label, g, a, b in zip(("dx", "dWg", "dWuT", "dWd"), got, want, dense):
+        rel, mx = check_y(g, a)
+        rel_d, _ = check_y(g, b)
+        print(f"{name} {label}: rel L2 {rel:.2e} (same active set), {rel_d:.2e} (dense definition)")
+    again = [t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, dy, hy)]
+    for g, h in zip(got, again):
+        assert np.array_equal(g.view(np.uint32), h.view(np.uint32))
 
 
 @pytest.mark.parametrize("name", list(SMALL))
