@@ -23,13 +23,14 @@
 //    (WuT_j gives u and the du term, Wd_j gives dh, Wg_j the dz term), two
 //    v_dot2_f32_bf16 wave reductions. Each unit's (h, dz, du) is written to
 //    an entry list laid out row by row.
-//  * The entry list is sorted by unit with a stable radix sort, so each
-//    unit's entries stay in row order; unit_grads then gives each unit one
-//    wave that walks its entries in that order and accumulates its three
+//  * The entry list is reordered by unit with a stable counting sort: the
+//    row kernel also counts entries per (block of kSortRows rows, unit); a
+//    column scan turns the counts into each (block, unit)'s first position;
+//    one workgroup per block then places its rows' entries in row order. So
+//    each unit's entries stay in row order, and unit_grads gives each unit
+//    one wave that walks them in that order and accumulates its three
 //    gradient rows from gathered x and dy rows. Every sum has a fixed order:
 //    results do not depend on scheduling.
-#include <hipcub/hipcub.hpp>
-
 #include "twell_device.hpp"
 #include "twell_internal.hpp"
 
@@ -38,6 +39,7 @@ namespace {
 
 constexpr int kRowsPerWG = 4;
 constexpr int kListCap = 512;
+constexpr int kSortRows = 64;  // rows per block of the counting sort
 
 // ------------------------------------------------------------- hybrid pack
 __global__ __launch_bounds__(64 * kRowsPerWG) void hybrid_pack_kernel(HybridArgs a) {
@@ -116,13 +118,71 @@ __global__ __launch_bounds__(1024) void scan_rows_kernel(const int32_t* count, i
   if (tid == 1023) row_off[M] = static_cast<int32_t>(min<int64_t>(s_sum[1023], INT32_MAX));
 }
 
-// Every entry slot starts past the last unit (the sort moves unused slots to
-// the end) and carries its own index as the sort's value.
-__global__ void init_entries_kernel(int32_t* keys, int32_t* perm_in, int64_t n, int F) {
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    keys[e] = F;
-    perm_in[e] = static_cast<int32_t>(e);
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[e] = v;
+}
+
+// unit_base[j] = entries of units below j (exclusive scan over F; one
+// workgroup of 1024 threads, each scanning a run of units); unit_base[F] = all.
+__global__ __launch_bounds__(1024) void scan_units_kernel(const int32_t* tot, int F, int32_t* unit_base) {
+  __shared__ int s_sum[1024];
+  const int tid = threadIdx.x;
+  const int per = (F + 1023) / 1024;
+  const int lo = min(F, tid * per), hi = min(F, lo + per);
+  int sum = 0;
+  for (int j = lo; j < hi; ++j) sum += tot[j];
+  s_sum[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += v;
+    __syncthreads();
+  }
+  int run = s_sum[tid] - sum;
+  for (int j = lo; j < hi; ++j) {
+    unit_base[j] = run;
+    run += tot[j];
+  }
+  if (tid == 1023) unit_base[F] = s_sum[1023];
+}
+
+// The per-block counts become first positions: (b, j) starts after unit j's
+// entries of blocks < b.
+__global__ void block_offsets_kernel(int32_t* hist, int nb, int F, const int32_t* unit_base) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= F) return;
+  int run = unit_base[j];
+  for (int b = 0; b < nb; ++b) {
+    const size_t k = static_cast<size_t>(b) * F + j;
+    const int c = hist[k];
+    hist[k] = run;
+    run += c;
+  }
+}
+
+// One workgroup per block of kSortRows rows: rows in order, a row's entries
+// (distinct units) in parallel; perm[position] = entry.
+__global__ __launch_bounds__(256) void place_entries_kernel(const int32_t* row_off, const int32_t* e_unit,
+                                                            const int32_t* offs, int M, int F, int64_t E_max,
+                                                            int32_t* perm) {
+  extern __shared__ int32_t s_off[];  // [F]
+  const int b = blockIdx.x;
+  for (int j = threadIdx.x; j < F; j += blockDim.x) s_off[j] = offs[static_cast<size_t>(b) * F + j];
+  __syncthreads();
+  const int r_end = min(M, (b + 1) * kSortRows);
+  for (int r = b * kSortRows; r < r_end; ++r) {
+    const int64_t e_lo = row_off[r], e_hi = min<int64_t>(row_off[r + 1], E_max);
+    for (int64_t e = e_lo + threadIdx.x; e < e_hi; e += blockDim.x) {
+      const int j = e_unit[e];
+      if (j < 0 || j >= F) continue;  // unused entry
+      const int pos = s_off[j];
+      s_off[j] = pos + 1;
+      perm[pos] = static_cast<int32_t>(e);
+    }
+    __syncthreads();  // the next row may hold the same units
   }
 }
 
@@ -140,10 +200,93 @@ struct Vec<4> {
   static constexpr int kWords = 2;
 };
 
+// The per-unit work of one token row r: entries lj/lg[0 .. m) (LDS), entry
+// numbers ent0 + k. Adds the row's dx terms to acc and writes each entry.
+template <int VEC, int NCH, int UNROLL>
+__device__ __forceinline__ void process_entries(const BackwardArgs& a, int r, const int* lj, const float* lg,
+                                                int m, int64_t ent0, const typename Vec<VEC>::T (&xv)[NCH],
+                                                const typename Vec<VEC>::T (&dyv)[NCH], float (&acc)[NCH][VEC]) {
+  using LoadT = typename Vec<VEC>::T;
+  constexpr int kW = Vec<VEC>::kWords;
+  constexpr int kChunk = 64 * VEC;
+  const int lane = threadIdx.x & 63;
+  for (int e = 0; e < m; e += UNROLL) {
+    int j[UNROLL];
+    float g[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int ee = min(e + u, m - 1);
+      j[u] = __builtin_amdgcn_readfirstlane(lj[ee]);
+      g[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg[ee])));
+    }
+    LoadT wu[UNROLL][NCH], wd[UNROLL][NCH], wg[UNROLL][NCH];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const size_t rb = static_cast<size_t>(j[u]) * a.d + lane * VEC;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        wu[u][ch] = *reinterpret_cast<const LoadT*>(a.WuT + rb + ch * kChunk);
+        wd[u][ch] = *reinterpret_cast<const LoadT*>(a.Wd + rb + ch * kChunk);
+        wg[u][ch] = *reinterpret_cast<const LoadT*>(a.Wg + rb + ch * kChunk);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      if (e + u < m) {  // uniform
+        float pu = 0.f, pd = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+          for (int q = 0; q < kW; ++q) {
+            pu = dot2_bf16(xv[ch][q], wu[u][ch][q], pu);
+            pd = dot2_bf16(dyv[ch][q], wd[u][ch][q], pd);
+          }
+        const float uu = wave_sum(pu);
+        const float dh = wave_sum(pd);
+        const float dz = dh * uu;
+        const float du = dh * g[u];
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+          for (int q = 0; q < kW; ++q) {
+            acc[ch][2 * q] = fmaf(dz, bf16_lo(wg[u][ch][q]), acc[ch][2 * q]);
+            acc[ch][2 * q + 1] = fmaf(dz, bf16_hi(wg[u][ch][q]), acc[ch][2 * q + 1]);
+            acc[ch][2 * q] = fmaf(du, bf16_lo(wu[u][ch][q]), acc[ch][2 * q]);
+            acc[ch][2 * q + 1] = fmaf(du, bf16_hi(wu[u][ch][q]), acc[ch][2 * q + 1]);
+          }
+        const int64_t ent = ent0 + e + u;
+        if (lane == 0 && ent < a.E_max) {
+          a.e_unit[ent] = j[u];
+          atomicAdd(&a.hist[static_cast<size_t>(r / kSortRows) * a.F + j[u]], 1);
+          atomicAdd(&a.unit_tot[j[u]], 1);
+          a.e_row[ent] = r;
+          a.e_h[ent] = g[u] * uu;
+          a.e_dz[ent] = dz;
+          a.e_du[ent] = du;
+        }
+      }
+    }
+  }
+}
+
+template <int VEC, int NCH>
+__device__ __forceinline__ void load_row(const uint16_t* base, int d, int r, typename Vec<VEC>::T (&v)[NCH]) {
+  using LoadT = typename Vec<VEC>::T;
+  const uint16_t* p = base + static_cast<size_t>(r) * d + (threadIdx.x & 63) * VEC;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) v[ch] = *reinterpret_cast<const LoadT*>(p + ch * 64 * VEC);
+}
+
+// Entries [from, e0 + n) of a row that are not produced are marked unused.
+__device__ __forceinline__ void mark_unused(const BackwardArgs& a, int64_t from, int64_t end) {
+  for (int64_t e = from + (threadIdx.x & 63); e < min<int64_t>(end, a.E_max); e += 64) a.e_unit[e] = -1;
+}
+
+// Rows held as sparse blocks: one wave per row. Reserve rows are left to
+// reserve_backward_kernel (rows the reserve could not hold get no gradient).
 template <int VEC, int NCH, int UNROLL>
 __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardArgs a) {
   using LoadT = typename Vec<VEC>::T;
-  constexpr int kW = Vec<VEC>::kWords;
   constexpr int kChunk = 64 * VEC;
   __shared__ int s_j[kRowsPerWG][kListCap];
   __shared__ float s_g[kRowsPerWG][kListCap];
@@ -153,23 +296,15 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
   const int r = blockIdx.x * kRowsPerWG + w;
   if (r >= a.M) return;
   const int n = a.h_count[r];
-  const bool reserve = n > a.K;
-  const float* dense = nullptr;
-  if (reserve) {
+  const int64_t e0 = a.row_off[r];
+  if (n > a.K) {
     const int slot = a.K > 0 ? a.h_idx[static_cast<size_t>(r) * a.K] : -1;
-    const int stored = min(*a.n_res, a.R);
-    if (slot < 0 || slot >= stored) return;  // not held by the reserve: no valid gradient
-    dense = a.res_vals + static_cast<size_t>(slot) * a.F;
+    if (slot < 0 || slot >= min(*a.n_res, a.R)) mark_unused(a, e0, e0 + n);
+    return;
   }
-
   LoadT xv[NCH], dyv[NCH];
-  const uint16_t* xr = a.x + static_cast<size_t>(r) * a.d + lane * VEC;
-  const uint16_t* dr = a.dy + static_cast<size_t>(r) * a.d + lane * VEC;
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    xv[ch] = *reinterpret_cast<const LoadT*>(xr + ch * kChunk);
-    dyv[ch] = *reinterpret_cast<const LoadT*>(dr + ch * kChunk);
-  }
+  load_row<VEC, NCH>(a.x, a.d, r, xv);
+  load_row<VEC, NCH>(a.dy, a.d, r, dyv);
   float acc[NCH][VEC];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch)
@@ -178,91 +313,14 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
 
   int* lj = s_j[w];
   float* lg = s_g[w];
-  const int64_t e0 = a.row_off[r];
-  int done = 0;      // entries of this row handled so far
-  int scan_at = 0;   // reserve rows: next unit to scan
-  while (done < n) {
-    // Stage up to kListCap of the row's (unit, g) in LDS.
-    int m = 0;
-    if (!reserve) {
-      m = min(kListCap, n - done);
-      for (int k = lane; k < m; k += 64) {
-        lj[k] = a.h_idx[static_cast<size_t>(r) * a.K + done + k];
-        lg[k] = a.h_vals[static_cast<size_t>(r) * a.K + done + k];
-      }
-    } else {
-      while (scan_at < a.F && m <= kListCap - 64) {
-        const int j = scan_at + lane;
-        const float g = j < a.F ? dense[j] : 0.f;
-        const uint64_t bal = __ballot(g > 0.f);
-        if (g > 0.f) {
-          const int at = m + static_cast<int>(mask_rank(bal));
-          lj[at] = j;
-          lg[at] = g;
-        }
-        m += __popcll(bal);
-        scan_at += 64;
-      }
-      m = min(m, n - done);
-      if (m == 0) break;  // fewer active units than the count says: stop rather than spin
+  for (int done = 0; done < n; done += kListCap) {
+    const int m = min(kListCap, n - done);
+    for (int k = lane; k < m; k += 64) {
+      lj[k] = a.h_idx[static_cast<size_t>(r) * a.K + done + k];
+      lg[k] = a.h_vals[static_cast<size_t>(r) * a.K + done + k];
     }
     wave_lds_sync();
-    for (int e = 0; e < m; e += UNROLL) {
-      int j[UNROLL];
-      float g[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int ee = min(e + u, m - 1);
-        j[u] = __builtin_amdgcn_readfirstlane(lj[ee]);
-        g[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lg[ee])));
-      }
-      LoadT wu[UNROLL][NCH], wd[UNROLL][NCH], wg[UNROLL][NCH];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const size_t rb = static_cast<size_t>(j[u]) * a.d + lane * VEC;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-          wu[u][ch] = *reinterpret_cast<const LoadT*>(a.WuT + rb + ch * kChunk);
-          wd[u][ch] = *reinterpret_cast<const LoadT*>(a.Wd + rb + ch * kChunk);
-          wg[u][ch] = *reinterpret_cast<const LoadT*>(a.Wg + rb + ch * kChunk);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        if (e + u < m) {  // uniform
-          float pu = 0.f, pd = 0.f;
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-            for (int q = 0; q < kW; ++q) {
-              pu = dot2_bf16(xv[ch][q], wu[u][ch][q], pu);
-              pd = dot2_bf16(dyv[ch][q], wd[u][ch][q], pd);
-            }
-          const float uu = wave_sum(pu);
-          const float dh = wave_sum(pd);
-          const float dz = dh * uu;
-          const float du = dh * g[u];
-#pragma unroll
-          for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-            for (int q = 0; q < kW; ++q) {
-              acc[ch][2 * q] = fmaf(dz, bf16_lo(wg[u][ch][q]), acc[ch][2 * q]);
-              acc[ch][2 * q + 1] = fmaf(dz, bf16_hi(wg[u][ch][q]), acc[ch][2 * q + 1]);
-              acc[ch][2 * q] = fmaf(du, bf16_lo(wu[u][ch][q]), acc[ch][2 * q]);
-              acc[ch][2 * q + 1] = fmaf(du, bf16_hi(wu[u][ch][q]), acc[ch][2 * q + 1]);
-            }
-          const int64_t ent = e0 + done + e + u;
-          if (lane == 0 && ent < a.E_max) {
-            a.keys[ent] = j[u];
-            a.e_row[ent] = r;
-            a.e_h[ent] = g[u] * uu;
-            a.e_dz[ent] = dz;
-            a.e_du[ent] = du;
-          }
-        }
-      }
-    }
-    done += m;
+    process_entries<VEC, NCH, UNROLL>(a, r, lj, lg, m, e0 + done, xv, dyv, acc);
     wave_lds_sync();
   }
 
@@ -275,18 +333,100 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
           make_float4(acc[ch][k], acc[ch][k + 1], acc[ch][k + 2], acc[ch][k + 3]);
 }
 
-// ------------------------------------------------------ per-unit gradients
-// First position of the sorted keys holding a value >= v (keys ascending).
-__device__ __forceinline__ int64_t lower_bound(const int32_t* keys, int64_t n, int v) {
-  int64_t lo = 0, hi = n;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (keys[mid] < v) lo = mid + 1;
-    else hi = mid;
+// Reserve rows: one workgroup of kResWaves waves per reserve slot. The dense
+// g row is compacted into an ascending (unit, g) list in LDS (each wave counts
+// a contiguous column range, a prefix over the waves places them); each wave
+// takes a contiguous run of the list; the waves' dx rows are added in wave
+// order through LDS (kRedCols columns at a time, reusing the list's space).
+constexpr int kResWaves = 8;
+constexpr int kRedCols = 4096;
+static_assert(kResWaves * kRedCols * 4 <= kBackwardMaxF * 8, "the reduction fits in the list's space");
+
+template <int VEC, int NCH, int UNROLL>
+__global__ __launch_bounds__(64 * kResWaves) void reserve_backward_kernel(BackwardArgs a) {
+  using LoadT = typename Vec<VEC>::T;
+  constexpr int kChunk = 64 * VEC;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kBackwardMaxF * 8];
+  __shared__ int s_cnt[kResWaves];
+  int* lj = reinterpret_cast<int*>(smem);
+  float* lg = reinterpret_cast<float*>(smem + kBackwardMaxF * 4);
+  float* red = reinterpret_cast<float*>(smem);  // [kResWaves][kRedCols], after the list is done
+
+  const int slot = blockIdx.x;
+  if (slot >= min(*a.n_res, a.R)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = a.res_rows[slot];
+  const int n = a.h_count[r];
+  const int64_t e0 = a.row_off[r];
+  const float* dense = a.res_vals + static_cast<size_t>(slot) * a.F;
+
+  // Compaction: wave w scans columns [w span, (w + 1) span).
+  const int span = ((a.F + 64 * kResWaves - 1) / (64 * kResWaves)) * 64;
+  const int c_lo = min(a.F, w * span), c_hi = min(a.F, c_lo + span);
+  int cnt = 0;
+  for (int c = c_lo; c < c_hi; c += 64) {
+    const int j = c + lane;
+    cnt += __popcll(__ballot(j < c_hi && dense[j] > 0.f));
   }
-  return lo;
+  if (lane == 0) s_cnt[w] = cnt;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < kResWaves; ++v) {
+    base += v < w ? s_cnt[v] : 0;
+    total += s_cnt[v];
+  }
+  for (int c = c_lo; c < c_hi; c += 64) {
+    const int j = c + lane;
+    const float g = j < c_hi ? dense[j] : 0.f;
+    const uint64_t bal = __ballot(g > 0.f);
+    if (g > 0.f) {
+      const int at = base + static_cast<int>(mask_rank(bal));
+      lj[at] = j;
+      lg[at] = g;
+    }
+    base += __popcll(bal);
+  }
+  __syncthreads();
+
+  const int m = min(total, n);
+  LoadT xv[NCH], dyv[NCH];
+  load_row<VEC, NCH>(a.x, a.d, r, xv);
+  load_row<VEC, NCH>(a.dy, a.d, r, dyv);
+  float acc[NCH][VEC];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[ch][k] = 0.f;
+  const int per = (m + kResWaves - 1) / kResWaves;
+  const int k_lo = min(m, w * per), k_hi = min(m, k_lo + per);
+  if (k_hi > k_lo) process_entries<VEC, NCH, UNROLL>(a, r, lj + k_lo, lg + k_lo, k_hi - k_lo, e0 + k_lo, xv, dyv, acc);
+  if (w == 0 && m < n) mark_unused(a, e0 + m, e0 + n);
+  __syncthreads();  // the list is no longer read
+
+  float* dxr = a.dx + static_cast<size_t>(r) * a.d;
+  for (int col0 = 0; col0 < a.d; col0 += kRedCols) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c = ch * kChunk + lane * VEC;  // this lane's first column of chunk ch
+      if (ch * kChunk >= col0 && ch * kChunk < col0 + kRedCols) {  // uniform
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) red[w * kRedCols + (c - col0) + k] = acc[ch][k];
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < kRedCols && col0 + c < a.d; c += 64 * kResWaves) {
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kResWaves; ++v) sum += red[v * kRedCols + c];
+      dxr[col0 + c] = sum;
+    }
+    __syncthreads();
+  }
 }
 
+// ------------------------------------------------------ per-unit gradients
 template <int VEC, int NCH, int UNROLL>
 __global__ __launch_bounds__(64 * kRowsPerWG) void unit_grads_kernel(BackwardArgs a) {
   using LoadT = typename Vec<VEC>::T;
@@ -295,13 +435,7 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void unit_grads_kernel(BackwardArg
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * kRowsPerWG + (threadIdx.x >> 6);
   if (j >= a.F) return;
-  int64_t lo = 0, hi = 0;
-  if (lane == 0) {
-    lo = lower_bound(a.keys_sorted, a.E_max, j);
-    hi = lower_bound(a.keys_sorted, a.E_max, j + 1);
-  }
-  lo = __builtin_amdgcn_readfirstlane(static_cast<int>(lo));
-  hi = __builtin_amdgcn_readfirstlane(static_cast<int>(hi));
+  const int64_t lo = a.unit_base[j], hi = a.unit_base[j + 1];
 
   float gd[NCH][VEC], gg[NCH][VEC], gu[NCH][VEC];
 #pragma unroll
@@ -376,6 +510,9 @@ template <int VEC, int NCH>
 hipError_t launch_rows(const BackwardArgs& a, hipStream_t s) {
   row_backward_kernel<VEC, NCH, row_unroll<NCH>()>
       <<<dim3((a.M + kRowsPerWG - 1) / kRowsPerWG), dim3(64 * kRowsPerWG), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.R == 0) return e;
+  reserve_backward_kernel<VEC, NCH, row_unroll<NCH>()><<<dim3(a.R), dim3(64 * kResWaves), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int VEC, int NCH>
@@ -406,12 +543,6 @@ hipError_t dispatch(const BackwardArgs& a, hipStream_t s) {
   return dispatch4<kUnits>(a.d / 256, a, s, std::make_integer_sequence<int, 8>{});
 }
 
-int key_bits(int F) {  // keys are 0..F
-  int b = 1;
-  while ((int64_t(1) << b) <= F) ++b;
-  return b;
-}
-
 }  // namespace
 
 bool backward_supports_d(int d) { return d >= 256 && d % 256 == 0 && (d % 512 == 0 ? d <= 8192 : d < 4096); }
@@ -423,28 +554,29 @@ hipError_t launch_hybrid_pack(const HybridArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t backward_sort_bytes(int64_t n, int F) {
-  size_t bytes = 0;
-  hipcub::DeviceRadixSort::SortPairs(nullptr, bytes, static_cast<const int32_t*>(nullptr),
-                                     static_cast<int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
-                                     static_cast<int32_t*>(nullptr), static_cast<int>(n), 0, key_bits(F),
-                                     hipStream_t(nullptr));
-  return bytes;
-}
+int backward_sort_blocks(int64_t M) { return static_cast<int>((M + kSortRows - 1) / kSortRows); }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s) {
+  const int nb = backward_sort_blocks(a.M);
+  const int64_t nh = static_cast<int64_t>(nb + 1) * a.F;  // per-block counts, then unit totals
   scan_rows_kernel<<<dim3(1), dim3(1024), 0, s>>>(a.h_count, a.M, a.row_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = std::min<int64_t>((a.E_max + 255) / 256, 4096);
-  init_entries_kernel<<<dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))), dim3(256), 0, s>>>(
-      a.keys, a.perm_in, a.E_max, a.F);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    fill_i32_kernel<<<dim3(static_cast<unsigned>(std::min<int64_t>((nh + 255) / 256, 4096))), dim3(256), 0, s>>>(
+        a.hist, nh, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.M > 0 && (e = dispatch<false>(a, s)) != hipSuccess) return e;
-  size_t bytes = a.sort_bytes;
-  e = hipcub::DeviceRadixSort::SortPairs(a.sort_tmp, bytes, a.keys, a.keys_sorted, a.perm_in, a.perm,
-                                         static_cast<int>(a.E_max), 0, key_bits(a.F), s);
-  if (e != hipSuccess) return e;
+  const dim3 ug((a.F + 255) / 256), ub(256);
+  scan_units_kernel<<<dim3(1), dim3(1024), 0, s>>>(a.unit_tot, a.F, a.unit_base);
+  block_offsets_kernel<<<ug, ub, 0, s>>>(a.hist, nb, a.F, a.unit_base);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (nb > 0) {
+    place_entries_kernel<<<dim3(nb), dim3(256), static_cast<size_t>(a.F) * 4, s>>>(a.row_off, a.e_unit, a.hist,
+                                                                                   a.M, a.F, a.E_max, a.perm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   return dispatch<true>(a, s);
 }
 

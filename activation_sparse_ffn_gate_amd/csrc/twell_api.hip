@@ -225,18 +225,19 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   return hip_status(twell::launch_dense(a, s));
 }
 
-// Workspace of twell_ffn_backward: row offsets, the entry list (keys, two
-// permutations, sorted keys, rows, h, dz, du) and the sort's scratch.
+// Workspace of twell_ffn_backward: row offsets, the counting sort's per-block
+// counts and unit offsets, and the entry list (unit, row, h, dz, du) with its
+// unit-major order.
 struct BwdLayout {
-  size_t row_off = 0, keys = 0, perm_in = 0, keys_sorted = 0, perm = 0, e_row = 0, e_h = 0, e_dz = 0, e_du = 0;
-  size_t sort = 0, sort_bytes = 0, total = 0;
+  size_t row_off = 0, hist = 0, unit_tot = 0, unit_base = 0, e_unit = 0, e_row = 0, perm = 0;
+  size_t e_h = 0, e_dz = 0, e_du = 0, total = 0;
   int64_t E_max = 0;
 };
 
 int check_bwd(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
   if (M < 0 || d <= 0 || F <= 0 || K < 1 || R < 0 || R > M) return TWELL_E_INVALID_ARG;
   if (M > kMaxM || F > kMaxF) return TWELL_E_INVALID_ARG;
-  if (!twell::backward_supports_d(int(d))) return TWELL_E_UNSUPPORTED;
+  if (!twell::backward_supports_d(int(d)) || F > twell::kBackwardMaxF) return TWELL_E_UNSUPPORTED;
   if (M * int64_t(K) + R * F >= (int64_t(1) << 31)) return TWELL_E_UNSUPPORTED;
   return TWELL_OK;
 }
@@ -252,16 +253,16 @@ BwdLayout bwd_layout(int64_t M, int64_t F, int32_t K, int64_t R) {
   L.E_max = M * int64_t(K) + R * F;
   const size_t e4 = size_t(L.E_max) * 4;
   L.row_off = take(size_t(M + 1) * 4);
-  L.keys = take(e4);
-  L.perm_in = take(e4);
-  L.keys_sorted = take(e4);
-  L.perm = take(e4);
+  // per-block counts and unit totals are one region (cleared together)
+  L.hist = take(size_t(twell::backward_sort_blocks(M) + 1) * size_t(F) * 4);
+  L.unit_tot = L.hist + size_t(twell::backward_sort_blocks(M)) * size_t(F) * 4;
+  L.unit_base = take(size_t(F + 1) * 4);
+  L.e_unit = take(e4);
   L.e_row = take(e4);
+  L.perm = take(e4);
   L.e_h = take(e4);
   L.e_dz = take(e4);
   L.e_du = take(e4);
-  L.sort_bytes = twell::backward_sort_bytes(L.E_max, int(F));
-  L.sort = take(std::max<size_t>(L.sort_bytes, 1));
   L.total = off;
   return L;
 }
@@ -312,7 +313,7 @@ int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu
                        void* workspace, size_t ws_bytes, void* stream) {
   if (!Wg || !WuT || !Wd || !hy || !hy->n_res || !dWg || !dWuT || !dWd) return TWELL_E_INVALID_ARG;
   if (M != 0 && (!x || !dy || !dx || !hy->idx || !hy->vals || !hy->count)) return TWELL_E_INVALID_ARG;
-  if (R != 0 && !hy->res_vals) return TWELL_E_INVALID_ARG;
+  if (R != 0 && (!hy->res_vals || !hy->res_rows)) return TWELL_E_INVALID_ARG;
   int st = check_bwd(M, d, F, K, R);
   if (st != TWELL_OK) return st;
   const BwdLayout L = bwd_layout(M, F, K, R);
@@ -327,6 +328,7 @@ int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu
   a.h_idx = hy->idx;
   a.h_vals = hy->vals;
   a.h_count = hy->count;
+  a.res_rows = hy->res_rows;
   a.res_vals = hy->res_vals;
   a.n_res = hy->n_res;
   a.M = int(M);
@@ -340,16 +342,15 @@ int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu
   a.dWu = dWuT;
   a.dWd = dWd;
   a.row_off = at<int32_t>(workspace, L.row_off);
-  a.keys = at<int32_t>(workspace, L.keys);
-  a.perm_in = at<int32_t>(workspace, L.perm_in);
-  a.keys_sorted = at<int32_t>(workspace, L.keys_sorted);
-  a.perm = at<int32_t>(workspace, L.perm);
+  a.hist = at<int32_t>(workspace, L.hist);
+  a.unit_tot = at<int32_t>(workspace, L.unit_tot);
+  a.unit_base = at<int32_t>(workspace, L.unit_base);
+  a.e_unit = at<int32_t>(workspace, L.e_unit);
   a.e_row = at<int32_t>(workspace, L.e_row);
+  a.perm = at<int32_t>(workspace, L.perm);
   a.e_h = at<float>(workspace, L.e_h);
   a.e_dz = at<float>(workspace, L.e_dz);
   a.e_du = at<float>(workspace, L.e_du);
-  a.sort_tmp = at<uint8_t>(workspace, L.sort);
-  a.sort_bytes = L.sort_bytes;
   return hip_status(twell::launch_backward(a, static_cast<hipStream_t>(stream)));
 }
 

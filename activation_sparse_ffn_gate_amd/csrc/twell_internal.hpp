@@ -117,19 +117,22 @@ struct BackwardArgs {
   const int32_t* h_idx;
   const float* h_vals;
   const int32_t* h_count;
+  const int32_t* res_rows;
   const float* res_vals;
   const int32_t* n_res;
   int M, d, F, K, R;
   int64_t E_max;  // entry capacity: M K + R F
   float *dx, *dWg, *dWu, *dWd;
-  int32_t* row_off;  // [M + 1]
-  int32_t *keys, *perm_in, *keys_sorted, *perm, *e_row;  // [E_max]
-  float *e_h, *e_dz, *e_du;                               // [E_max]
-  void* sort_tmp;
-  size_t sort_bytes;
+  int32_t* row_off;    // [M + 1]
+  int32_t* hist;       // [sort blocks, F] entry counts, then first positions
+  int32_t* unit_tot;   // [F]
+  int32_t* unit_base;  // [F + 1]
+  int32_t *e_unit, *e_row, *perm;  // [E_max]
+  float *e_h, *e_dz, *e_du;        // [E_max]
 };
+constexpr int kBackwardMaxF = 16384;  // the entry placement keeps one counter per unit in LDS (64 KB)
 bool backward_supports_d(int d);
-size_t backward_sort_bytes(int64_t n, int F);
+int backward_sort_blocks(int64_t M);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 
 // Row gather: out[i] = W[src[i]] for 0 <= src[i] < F, else a zero row.

@@ -95,7 +95,7 @@ def parse():
     ap.add_argument("--workload", default="ffn1p5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
-    ap.add_argument("--only", choices=["forward", "gate", "fused", "sliced", "fallback", "dense", "copy"],
+    ap.add_argument("--only", choices=["forward", "gate", "fused", "sliced", "fallback", "dense", "copy", "backward"],
                     default=None,
                     help="run only this leg (for profiler runs); prints a short line")
     ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
@@ -246,6 +246,76 @@ def layer_sweep(dev, names, steps, warmup, graphs=False):
     return out
 
 
+def dense_backward_torch(x, Wg, WuT, Wd, dy):
+    """The dense gated FFN's backward on hipBLASLt through torch (bf16
+    products, fp32 accumulate), from the forward's saved z, u: dH = dy Wd^T,
+    dZ = dH u [z > 0], dU = dH ReLU(z), dx = [dZ dU] [Wg; WuT],
+    d[Wg; WuT] = [dZ dU]^T x, dWd = h^T dy."""
+    import torch
+
+    F = Wg.shape[0]
+    Wgu = torch.cat([Wg, WuT], 0).contiguous()
+    zu = torch.nn.functional.linear(x, Wgu)
+    z, u = zu[:, :F], zu[:, F:]
+    h = (torch.relu(z) * u).contiguous()
+    mask = (z > 0).to(x.dtype)
+    WdT = Wd.t().contiguous()
+    xT = x.t().contiguous()
+    dyT = dy.t().contiguous()
+
+    def run():
+        dH = dy @ WdT
+        dZU = torch.cat([dH * u * mask, dH * torch.relu(z)], 1)
+        dx = dZU @ Wgu
+        dWgu = (dZU.t().contiguous() @ x)
+        dWd = (h.t().contiguous() @ dy)
+        return dx, dWgu, dWd
+
+    return run
+
+
+def training_backward(dev, name, K, R, steps, warmup):
+    """Hybrid pack and sparse backward against the dense backward (hipBLASLt)."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+    from synth import WORKLOADS, make_inputs, make_upstream_grad
+
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    td = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+    x, Wg, WuT, Wd = (td(a) for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+    dy = td(make_upstream_grad(w))
+    stream = torch.cuda.current_stream(dev)
+    p = tw.gate_pack(x, Wg, w.T, w.T)  # C = T: every active unit kept
+    hy = tw.Hybrid.empty(w.M, w.F, K, R, dev)
+    ws = tw.Workspace(dev)
+    outs = (torch.empty((w.M, w.d), dtype=torch.float32, device=dev),
+            *(torch.empty((w.F, w.d), dtype=torch.float32, device=dev) for _ in range(3)))
+    pack = lambda: tw.hybrid_pack(p, w.F, K, R, out=hy)  # noqa: E731
+    bwd = lambda: tw.ffn_backward(x, Wg, WuT, Wd, dy, hy, workspace=ws, out=outs)  # noqa: E731
+    dense = dense_backward_torch(x, Wg, WuT, Wd, dy)
+    res = {}
+    for key, fn in (("hybrid_pack", pack), ("sparse_backward", bwd), ("dense_backward_hipblaslt", dense)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        res[key] = time_loop(fn, steps, stream)
+    pack()
+    torch.cuda.synchronize()
+    count = hy.count.cpu().numpy()
+    flops_dense = 12.0 * w.M * w.d * w.F
+    out = {"workload": name, "M": w.M, "d": w.d, "F": w.F, "K": K, "R": R,
+           "reserve_rows": int(hy.n_res.item()), "entries": int(count.sum()),
+           "dense_backward_tflops": round(flops_dense / (res["dense_backward_hipblaslt"] * 1e-3) / 1e12, 1)}
+    out.update({f"{k}_ms": round(v, 5) for k, v in res.items()})
+    out["speedup_vs_dense"] = round(res["dense_backward_hipblaslt"] / res["sparse_backward"], 3)
+    del x, Wg, WuT, Wd, dy, p, hy, ws, outs, dense
+    torch.cuda.empty_cache()
+    return out
+
+
 def dead_unit_compaction(dev, name, steps, warmup):
     """The layer with its never-active units dropped (activity taken over the
     layer's own batch), against the full layer: forward and gate times, the
@@ -380,6 +450,22 @@ def main():
     y_dense = torch.empty_like(y)
     dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y_dense, workspace=ws_dense)  # noqa: E731
 
+    if args.only == "backward":  # hybrid pack once, then the timed sparse backward
+        from synth import make_upstream_grad
+
+        dy = td(make_upstream_grad(w))
+        p_full = tw.gate_pack(x, Wg, w.T, w.T)
+        hy = tw.hybrid_pack(p_full, w.F, 64, min(512, w.M))
+        ws_b = tw.Workspace(dev)
+        outs = (torch.empty((w.M, w.d), dtype=torch.float32, device=dev),
+                *(torch.empty((w.F, w.d), dtype=torch.float32, device=dev) for _ in range(3)))
+        fn = lambda: tw.ffn_backward(x, Wg, WuT, Wd, dy, hy, workspace=ws_b, out=outs)  # noqa: E731
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = time_loop(fn, args.steps, stream)
+        print(json.dumps({"only": args.only, "ms_per_call": round(ms, 5), "steps": args.steps}))
+        return 0
     if args.only is not None:
         if args.only == "copy":
             n = args.copy_mb * (1 << 20) // 4
@@ -510,6 +596,8 @@ def main():
         decode = sorted((k for k in _W if k.startswith("decode_")), key=lambda k: _W[k].M)
         out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4, graphs=True)
         out["dead_unit_compaction"] = dead_unit_compaction(dev, "ffn1p5b_heavytail", 2 * args.sweep_steps, 3)
+        out["training_backward"] = [training_backward(dev, n, 64, 512, 2 * args.sweep_steps, 2)
+                                    for n in ("ffn1p5b", "ffn1p5b_heavytail")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))

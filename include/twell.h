@@ -233,8 +233,8 @@ size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K
  * units enter (their dZ, dU and h are the only non-zeros): per token, row
  * gathers of WuT, Wd and Wg; per unit, gathers of the x and dy rows of its
  * tokens in token order. Sums have a fixed order (deterministic).
- * d: multiples of 512 up to 8192, or odd multiples of 256 below 4096.
- * M K + R F < 2^31. workspace >= twell_backward_workspace_bytes(...). */
+ * d: multiples of 512 up to 8192, or odd multiples of 256 below 4096;
+ * F <= 16384; M K + R F < 2^31. workspace >= twell_backward_workspace_bytes(...). */
 int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
                        const uint16_t* dy, const twell_hybrid* hy, int64_t M, int64_t d, int64_t F,
                        int32_t K, int64_t R, float* dx, float* dWg, float* dWuT, float* dWd,

@@ -213,7 +213,8 @@ def test_backward_validation():
     L = tw.lib()
     M, d, F, T, K, R = 64, 256, 1024, 64, 8, 4
     ws = tw.backward_workspace_bytes(M, d, F, K, R)
-    assert ws >= 8 * 4 * (M * K + R * F)
+    assert ws >= 6 * 4 * (M * K + R * F)
+    assert tw.backward_workspace_bytes(M, d, 32768, K, R) == 0  # F past the placement's LDS counters
     assert tw.backward_workspace_bytes(M, 320, F, K, R) == 0      # d not supported
     assert tw.backward_workspace_bytes(M, d, F, 0, R) == 0        # K >= 1
     assert tw.backward_workspace_bytes(M, d, F, K, M + 1) == 0    # R <= M
