@@ -459,3 +459,46 @@ def test_full_size(name):
     tw.dense_fallback(x, Wg, WuT, Wd, p, yf)
     rel_f, _ = check_y(yf.cpu().numpy()[rows], Ys)
     print(f"[full] {name}: fused form sampled rel L2 {rel_f:.2e}")
+
+
+@pytest.mark.parametrize("name", ["ffn1p5b", "ffn1p5b_heavytail"])
+def test_backward_full_size(name):
+    """The training backward at full size (K = 64, R = 512, as bench.py runs
+    it): counts and sampled rows' blocks of the hybrid format bit-exact,
+    dx on sampled rows and the three weight gradients on sampled units against
+    the oracle on the kernel's active set (its fp32 z decides, as in the
+    packing)."""
+    inp = make_inputs(WORKLOADS[name])
+    w = inp.workload
+    K, R = 64, 512
+    print(f"[full-bwd] {name} M={w.M} d={w.d} F={w.F} K={K} R={R}", flush=True)
+    x, Wg, WuT, Wd = dev(inp)
+    dy_bits = make_upstream_grad(w)
+    dy = to_device(dy_bits, DEV)
+    z = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV)
+    p = tw.gate_pack(x, Wg, w.T, w.T, z_debug=z)
+    hy = tw.hybrid_pack(p, w.F, K, R)
+    dx, dWg, dWu, dWd = (t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, dy, hy))
+    z32 = z.cpu().numpy()
+    del z
+    count = hy.count.cpu().numpy()
+    assert np.array_equal(count, (z32 > 0).sum(axis=1))
+    n_res = int(hy.n_res.item())
+    assert n_res == int((count > K).sum()) and n_res <= R
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([rng.choice(w.M, 48, replace=False),
+                                     np.flatnonzero(count > K)[:16]]))  # reserve rows too
+    ref_rows = O.hybrid_pack(z32[rows], K)
+    idx = hy.idx.cpu().numpy()
+    for i, r in enumerate(rows):
+        if count[r] <= K:
+            assert np.array_equal(idx[r, :count[r]], ref_rows.idx[i, :count[r]])
+    hy_rows = O.hybrid_pack(z32[rows], w.F)  # every sampled row as one block
+    want_dx = O.ffn_backward_from_hybrid(hy_rows, inp.x[rows], inp.Wg, inp.WuT, inp.Wd, dy_bits[rows])[0]
+    rel, _ = check_y(dx[rows], want_dx)
+    units = np.unique(rng.choice(w.F, 48, replace=False))
+    hy_units = O.hybrid_pack(z32[:, units], len(units))  # the sampled units alone
+    _, gWg, gWu, gWd = O.ffn_backward_from_hybrid(hy_units, inp.x, inp.Wg[units], inp.WuT[units],
+                                                  inp.Wd[units], dy_bits)
+    rels = [check_y(got[units], want)[0] for got, want in ((dWg, gWg), (dWu, gWu), (dWd, gWd))]
+    print(f"[full-bwd] {name}: reserve rows {n_res}, dx rel L2 {rel:.2e}, dW rel L2 {max(rels):.2e}")
