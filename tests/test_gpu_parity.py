@@ -55,6 +55,8 @@ SMALL = {
     "few_rows_d768": scaled(WORKLOADS["ffn1p5b"], M=5, d=768, F=2048),
     "few_rows_d2560": scaled(WORKLOADS["ffn2b_zipf"], M=7, d=2560, F=2560),
     "few_rows_dense30": scaled(WORKLOADS["sweep_p11pct"], M=9, d=512, F=8192, T=64, C=64, mean_nnz=2458.0),
+    # the headline's d: the backward's column-sliced weight-gradient kernel
+    "d2048_small": scaled(WORKLOADS["ffn1p5b"], M=200, d=2048, F=1024, mean_nnz=24.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
@@ -278,6 +280,7 @@ TRAIN = {
     "heavytail_small": (40, 1100),
     "zipf_small": (16, 520),
     "few_rows_d768": (6, 5),
+    "d2048_small": (20, 200),
 }
 
 
