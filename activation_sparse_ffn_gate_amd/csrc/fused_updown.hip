@@ -184,10 +184,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
   const int C = a.C;
   const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
 
-  // Every wave reads the counts, so all of them take the same decision.
+  // Every wave reads the counts, so all of them take the same decision. An
+  // overflow row is left to the dense fallback, unless its overflowing tiles
+  // were spilled: then their units are read from the spilled z.
   bool over = false;
   for (int t = lane; t < nT; t += 64) over |= cnt_row[t] > C;
-  if (__ballot(over) != 0) return;  // overflow row: owned by the dense fallback
+  if (__ballot(over) != 0 && a.spill == nullptr) return;
 
   LoadT xv[NCH];
   const uint16_t* xr = a.x + static_cast<size_t>(row) * a.d + lane * VEC;
@@ -214,11 +216,28 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
     const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
     for (int base = 0; base < total; base += kWideCap) {
       // Fill: lane t of wave w copies slots s = s_lo + w, s_lo + w + kWideWaves, ...
+      // A spilled tile (count > C) is read by wave 0: its active units in
+      // ascending order, the s-th one going to slot s.
       const int s_lo = max(0, base - off);
       const int s_hi = min(c, base + kWideCap - off);
-      for (int s = s_lo + w; s < s_hi; s += kWideWaves) {
-        s_j[off + s - base] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
-        s_h[off + s - base] = a.vals[slot0 + s];
+      if (c <= C) {
+        for (int s = s_lo + w; s < s_hi; s += kWideWaves) {
+          s_j[off + s - base] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
+          s_h[off + s - base] = a.vals[slot0 + s];
+        }
+      } else if (w == 0 && s_lo < s_hi) {
+        const float* seg = a.spill + (static_cast<size_t>(row) * nT + t) * a.T;
+        int k = 0;
+        for (int u = 0; u < a.T && k < s_hi; ++u) {
+          const float z = seg[u];
+          if (z > 0.f) {
+            if (k >= s_lo) {
+              s_j[off + k - base] = t * a.T + u;
+              s_h[off + k - base] = z;
+            }
+            ++k;
+          }
+        }
       }
       __syncthreads();
       const int n = min(kWideCap, total - base);

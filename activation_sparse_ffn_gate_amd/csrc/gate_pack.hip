@@ -330,6 +330,7 @@ __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   if (a.M <= kSkinnyMaxM) return launch_gate_pack_skinny(a, s);
+  if (a.spill != nullptr) return hipErrorInvalidValue;  // only the small-batch kernel spills
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.F + kBN - 1) / kBN;
   const dim3 grid(tiles_m * tiles_n), block(256);

@@ -235,9 +235,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
       const uint32_t ulocal = static_cast<uint32_t>(wt * 32 + r);  // index inside the tile
       static_for<0, 16 * RB>([&](auto I) {
         constexpr int b = decltype(I)::value / 16, v = decltype(I)::value % 16;
+        constexpr int t_lo = 32 * b + acc_row(v, 0), t_hi = 32 * b + acc_row(v, 1);
+        if (a.spill != nullptr) {  // every z of a (token, tile) that overflows, active or not
+          const int t_own = half ? __builtin_amdgcn_readlane(tot, t_hi) : __builtin_amdgcn_readlane(tot, t_lo);
+          const int row = m0 + 32 * b + acc_row(v, half);
+          if (t_own > C && row < a.M)
+            a.spill[(static_cast<size_t>(row) * nT + tile) * kT + ulocal] = acc[b][v];
+        }
         const uint64_t bq = bal[b][v];
         if (bq == 0) return;
-        constexpr int t_lo = 32 * b + acc_row(v, 0), t_hi = 32 * b + acc_row(v, 1);
         const uint32_t pre_lo = __builtin_amdgcn_readlane(pre, t_lo);
         const uint32_t pre_hi = __builtin_amdgcn_readlane(pre, t_hi);
         const uint32_t rank = half ? __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32), 0u)

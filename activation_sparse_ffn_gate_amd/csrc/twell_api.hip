@@ -136,7 +136,7 @@ twell_packed packed_in_ws(void* ws, const Layout& L) {
 
 int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F, int32_t T,
                    int32_t C, const twell_packed* out, float* z_debug, uint32_t* ctrl,
-                   hipStream_t s, uint32_t* col_active = nullptr) {
+                   hipStream_t s, uint32_t* col_active = nullptr, float* spill = nullptr) {
   if (M == 0) return hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
   twell::GateArgs a;
   a.x = x;
@@ -154,11 +154,13 @@ int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, 
   a.ctrl = ctrl;
   a.z_debug = z_debug;
   a.col_active = col_active;
+  a.spill = spill;
   return hip_status(twell::launch_gate_pack(a, s));
 }
 
 int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
-               int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s) {
+               int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s,
+               const float* spill = nullptr) {
   if (M == 0) return TWELL_OK;
   twell::FusedArgs a;
   a.x = x;
@@ -173,6 +175,7 @@ int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const
   a.T = T;
   a.C = C;
   a.y = y;
+  a.spill = spill;
   return hip_status(twell::launch_fused_updown(a, s));
 }
 
@@ -423,12 +426,18 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
+  if (M < twell::kFewRows) {
+    // Few rows: the small-batch gate spills the z of every overflowing
+    // (row, tile) into the fallback's region, and the fused kernel (a
+    // workgroup per row) does overflow rows from it: two launches in all.
+    float* spill = at<float>(workspace, L.h_hi);  // M F floats: the region holds 2 M F bf16
+    st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill);
+    if (st != TWELL_OK) return st;
+    return fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s, spill);
+  }
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
-  // The sliced form needs two launches and 8 waves per row; below a few rows
-  // the single fused launch is quicker (measured: 12.8 vs 17.2 us at M = 1,
-  // d = 2048, F = 8192; equal at M = 16).
-  if (M >= twell::kFewRows && twell::sliced_supports(d, F))
+  if (twell::sliced_supports(d, F))
     st = sliced_impl(x, WuT, Wd, &p, M, d, F, T, C, at<uint8_t>(workspace, L.part), y, s);
   else
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);

@@ -27,6 +27,7 @@ struct GateArgs {
   uint32_t* ctrl;   // kCtrlBytes, then flags[M]
   float* z_debug;   // nullable
   uint32_t* col_active;  // nullable: bit j % 32 of word j / 32 ORed with "some row has z_j > 0"
+  float* spill;          // nullable, small-batch kernel only: [M, F/T, T] raw z of every (row, tile) with count > C
 };
 
 struct FusedArgs {
@@ -38,6 +39,7 @@ struct FusedArgs {
   const uint16_t* counts;
   int M, d, F, T, C;
   float* y;
+  const float* spill;  // nullable: rows with a tile count > C are done from it (else left to the fallback)
 };
 
 // Dense gated FFN over a list of rows (all rows, or the overflow rows).

@@ -141,10 +141,13 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
                          int64_t F, float* y, void* ctrl, size_t ctrl_bytes, void* workspace,
                          size_t ws_bytes, void* stream);
 
-/* The whole sparse forward: twell_gate_pack, then twell_sliced_updown (or
- * twell_fused_updown below 256 rows and for the d that the sliced form does not
- * support), then twell_dense_fallback, on one stream, with the packing kept in
- * the workspace (see twell_packed_view). y [M, d] fp32 is fully written.
+/* The whole sparse forward, on one stream, with the packing kept in the
+ * workspace (see twell_packed_view); y [M, d] fp32 is fully written.
+ * From 256 rows: twell_gate_pack, then twell_sliced_updown (twell_fused_updown
+ * for the d that the sliced form does not support), then twell_dense_fallback.
+ * Below 256 rows: the gate also keeps every z of each (row, tile) whose count
+ * exceeds C in the workspace, and the fused kernel does overflow rows from it
+ * (their whole active set, still only gathers): two launches, no fallback.
  * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                       const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,

@@ -55,7 +55,7 @@ SMALL = {
     "few_rows_d768": scaled(WORKLOADS["ffn1p5b"], M=5, d=768, F=2048),
     "few_rows_d2560": scaled(WORKLOADS["ffn2b_zipf"], M=7, d=2560, F=2560),
     "few_rows_dense30": scaled(WORKLOADS["sweep_p11pct"], M=9, d=512, F=8192, T=64, C=64, mean_nnz=2458.0),
-    # the headline's d: the backward's column-sliced weight-gradient kernel
+    # the headline's d = 2048 through the small-batch forward and the training path
     "d2048_small": scaled(WORKLOADS["ffn1p5b"], M=200, d=2048, F=1024, mean_nnz=24.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
@@ -122,8 +122,10 @@ def sliced_ok(d):
 def test_components_compose(name):
     """gate_pack + (sliced or fused) up/down + dense_fallback == ffn_forward,
     bit for bit; the up/down kernels leave overflow rows alone; packed_view
-    shows the packing."""
-    inp, _, _, _ = small_case(name)
+    shows the packing. Below 256 rows the forward does overflow rows from the
+    gate's spilled z instead of the fallback: there the rows that fit are
+    compared bit for bit and the overflow rows against the definition."""
+    inp, _, _, Y = small_case(name)
     w = inp.workload
     x, Wg, WuT, Wd = dev(inp)
     y_full = tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=nan_y(w.M, w.d))
@@ -140,7 +142,14 @@ def test_components_compose(name):
     assert np.isnan(yh[ovf]).all(), "up/down kernel wrote an overflow row"
     assert np.isfinite(yh[fit]).all()
     tw.dense_fallback(x, Wg, WuT, Wd, p, y)
-    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_full.cpu().numpy().view(np.uint32))
+    yc, yf = y.cpu().numpy(), y_full.cpu().numpy()
+    if w.M >= 256:
+        assert np.array_equal(yc.view(np.uint32), yf.view(np.uint32))
+    else:
+        assert np.array_equal(yc[fit].view(np.uint32), yf[fit].view(np.uint32))
+        if len(ovf):
+            rel, _ = check_y(yf[ovf], Y[ovf])
+            print(f"{name}: {len(ovf)} overflow rows from the spill, rel L2 {rel:.2e}")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
