@@ -322,7 +322,7 @@ constexpr int unroll_for() {
 
 template <int VEC, int NCH>
 hipError_t launch_vec(const FusedArgs& a, hipStream_t s) {
-  if (a.M < kFewRows) {
+  if (a.M <= kFewRows) {
     // d = 64 * VEC * NCH; NQ 4-column groups per lane cover it with 8 waves
     constexpr int kD = 64 * VEC * NCH;
     constexpr int kNQ = (kD / 4 + 64 * kWideWaves - 1) / (64 * kWideWaves);

@@ -426,8 +426,8 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
-  if (M < twell::kFewRows) {
-    // Few rows: the small-batch gate spills the z of every overflowing
+  if (M <= twell::kFewRows) {
+    // Few rows (the small-batch gate's range): it spills the z of every overflowing
     // (row, tile) into the fallback's region, and the fused kernel (a
     // workgroup per row) does overflow rows from it: two launches in all.
     float* spill = at<float>(workspace, L.h_hi);  // M F floats: the region holds 2 M F bf16

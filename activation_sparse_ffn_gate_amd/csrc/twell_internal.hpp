@@ -97,7 +97,7 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 // d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
 bool sliced_supports(int64_t d, int64_t F);
 SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C);
-constexpr int kFewRows = 256;  // below: the fused form with a workgroup per token, also in the forward
+constexpr int kFewRows = 256;  // up to here: the fused form with a workgroup per token, also in the forward
 // Hybrid training format from a complete TwELL packing (C == T).
 struct HybridArgs {
   const float* vals;

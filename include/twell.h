@@ -143,9 +143,9 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
 
 /* The whole sparse forward, on one stream, with the packing kept in the
  * workspace (see twell_packed_view); y [M, d] fp32 is fully written.
- * From 256 rows: twell_gate_pack, then twell_sliced_updown (twell_fused_updown
+ * Above 256 rows: twell_gate_pack, then twell_sliced_updown (twell_fused_updown
  * for the d that the sliced form does not support), then twell_dense_fallback.
- * Below 256 rows: the gate also keeps every z of each (row, tile) whose count
+ * Up to 256 rows: the gate also keeps every z of each (row, tile) whose count
  * exceeds C in the workspace, and the fused kernel does overflow rows from it
  * (their whole active set, still only gathers): two launches, no fallback.
  * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */

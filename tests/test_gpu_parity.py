@@ -122,7 +122,7 @@ def sliced_ok(d):
 def test_components_compose(name):
     """gate_pack + (sliced or fused) up/down + dense_fallback == ffn_forward,
     bit for bit; the up/down kernels leave overflow rows alone; packed_view
-    shows the packing. Below 256 rows the forward does overflow rows from the
+    shows the packing. Up to 256 rows the forward does overflow rows from the
     gate's spilled z instead of the fallback: there the rows that fit are
     compared bit for bit and the overflow rows against the definition."""
     inp, _, _, Y = small_case(name)
@@ -133,8 +133,8 @@ def test_components_compose(name):
     p = tw.gate_pack(x, Wg, w.T, w.C)
     g = host_packing(p)
     assert np.array_equal(view["counts"], g["counts"]) and np.array_equal(view["ovf"], g["ovf"])
-    # the forward's choice: the sliced form from 256 rows on, where d allows it
-    updown = tw.sliced_updown if (w.M >= 256 and sliced_ok(w.d)) else tw.fused_updown
+    # the forward's choice: the sliced form above 256 rows, where d allows it
+    updown = tw.sliced_updown if (w.M > 256 and sliced_ok(w.d)) else tw.fused_updown
     y = updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
     yh = y.cpu().numpy()
     ovf = g["ovf"]
@@ -143,7 +143,7 @@ def test_components_compose(name):
     assert np.isfinite(yh[fit]).all()
     tw.dense_fallback(x, Wg, WuT, Wd, p, y)
     yc, yf = y.cpu().numpy(), y_full.cpu().numpy()
-    if w.M >= 256:
+    if w.M > 256:
         assert np.array_equal(yc.view(np.uint32), yf.view(np.uint32))
     else:
         assert np.array_equal(yc[fit].view(np.uint32), yf[fit].view(np.uint32))
@@ -176,8 +176,8 @@ def test_updown_kernels_match_definition(name):
 
 @pytest.mark.parametrize("name", ["uniform_ragged", "zipf_small", "long_rows", "fused_only_d2304", "few_rows_d2560"])
 def test_fused_forms_agree(name):
-    """The fused kernel runs a workgroup per token below 256 rows and a wave
-    per token from 256 on; rows are independent and both forms take every
+    """The fused kernel runs a workgroup per token up to 256 rows and a wave
+    per token above; rows are independent and both forms take every
     product and sum in the same order, so a batch's first rows alone give the
     same bits as the whole batch. The case's rows are repeated up to 300."""
     inp, _, _, _ = small_case(name)
