@@ -333,17 +333,18 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
           make_float4(acc[ch][k], acc[ch][k + 1], acc[ch][k + 2], acc[ch][k + 3]);
 }
 
-// Reserve rows: one workgroup of kResWaves waves per reserve slot. The dense
+// Reserve rows: one workgroup of kResWaves waves per reserve slot (long rows:
+// many units' gathers in flight at once). The dense
 // g row is compacted into an ascending (unit, g) list in LDS (each wave counts
 // a contiguous column range, a prefix over the waves places them); each wave
 // takes a contiguous run of the list; the waves' dx rows are added in wave
 // order through LDS (kRedCols columns at a time, reusing the list's space).
-constexpr int kResWaves = 8;
-constexpr int kRedCols = 4096;
-static_assert(kResWaves * kRedCols * 4 <= kBackwardMaxF * 8, "the reduction fits in the list's space");
-
-template <int VEC, int NCH, int UNROLL>
+// kResWaves waves: 16 while a wave's rows fit in 128 registers (d <= 2048),
+// else 8; the reduction takes kRedCols = 32768 / kResWaves columns a pass.
+template <int VEC, int NCH, int UNROLL, int kResWaves>
 __global__ __launch_bounds__(64 * kResWaves) void reserve_backward_kernel(BackwardArgs a) {
+  constexpr int kRedCols = 32768 / kResWaves;
+  static_assert(kResWaves * kRedCols * 4 <= kBackwardMaxF * 8, "the reduction fits in the list's space");
   using LoadT = typename Vec<VEC>::T;
   constexpr int kChunk = 64 * VEC;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBackwardMaxF * 8];
@@ -512,7 +513,10 @@ hipError_t launch_rows(const BackwardArgs& a, hipStream_t s) {
       <<<dim3((a.M + kRowsPerWG - 1) / kRowsPerWG), dim3(64 * kRowsPerWG), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.R == 0) return e;
-  reserve_backward_kernel<VEC, NCH, row_unroll<NCH>()><<<dim3(a.R), dim3(64 * kResWaves), 0, s>>>(a);
+  // 16 waves of a workgroup leave 128 registers a wave: one unit at a time
+  constexpr int kWaves = VEC * NCH <= 32 ? 16 : 8;
+  reserve_backward_kernel<VEC, NCH, kWaves == 16 ? 1 : row_unroll<NCH>(), kWaves>
+      <<<dim3(a.R), dim3(64 * kWaves), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int VEC, int NCH>
