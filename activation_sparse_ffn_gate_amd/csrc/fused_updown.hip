@@ -18,6 +18,7 @@
 // Several units are in flight per wave (their row loads are issued together)
 // to keep enough bytes outstanding. Rows whose packing overflowed (some tile
 // count > C) are skipped; the dense fallback writes them.
+#include <algorithm>
 #include <type_traits>
 
 #include "twell_device.hpp"
@@ -166,6 +167,8 @@ __global__ __launch_bounds__(256) void fused_updown_kernel(FusedArgs a) {
 // one-wave form, so both forms give the same bits.
 constexpr int kWideWaves = 8;
 constexpr int kWideCap = 1024;  // list entries per round
+constexpr int kSplitMinEntries = 384;  // longer rows may be cut into parts
+constexpr int kSplitChunk = 192;       // entries per part at least
 
 template <int VEC, int NCH, int UP, int NQ, int DN>
 __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(FusedArgs a) {
@@ -176,9 +179,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
   __shared__ int s_j[kWideCap];
   __shared__ float s_h[kWideCap];  // gate value, then h
 
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = blockIdx.x;
+  // splits > 1: workgroup k M + row takes part k of a long row (the first M
+  // workgroups are the whole of every short row).
+  const int row = blockIdx.x % a.M;
+  const int part_k = blockIdx.x / a.M;
 
   const int nT = a.F / a.T;
   const int C = a.C;
@@ -188,8 +195,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
   // overflow row is left to the dense fallback, unless its overflowing tiles
   // were spilled: then their units are read from the spilled z.
   bool over = false;
-  for (int t = lane; t < nT; t += 64) over |= cnt_row[t] > C;
+  int row_total = 0;
+  for (int t = lane; t < nT; t += 64) {
+    const int c = cnt_row[t];
+    over |= c > C;
+    row_total += c;
+  }
   if (__ballot(over) != 0 && a.spill == nullptr) return;
+  // A long row is cut into P contiguous runs of its ascending unit list, run k
+  // done by part k; each part's y row goes to a partial buffer and the last
+  // part to finish adds them in part order.
+  row_total = __builtin_amdgcn_readlane(wave_inclusive_scan(row_total), 63);
+  const int P = (a.splits > 1 && row_total > kSplitMinEntries)
+                    ? min(a.splits, (row_total + kSplitChunk - 1) / kSplitChunk)
+                    : 1;
+  if (part_k >= P) return;
+  const int e_lo = static_cast<int>(static_cast<int64_t>(part_k) * row_total / P);
+  const int e_hi = static_cast<int>(static_cast<int64_t>(part_k + 1) * row_total / P);
 
   LoadT xv[NCH];
   const uint16_t* xr = a.x + static_cast<size_t>(row) * a.d + lane * VEC;
@@ -207,6 +229,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
   const char* wdb = reinterpret_cast<const char*>(a.Wd);
 
+  int gbase = 0;  // entries of the row before this tile group
   for (int t0 = 0; t0 < nT; t0 += 64) {
     const int t = t0 + lane;
     const int c = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
@@ -214,10 +237,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
     const int total = __builtin_amdgcn_readlane(incl, 63);
     const int off = incl - c;
     const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
+    if (gbase + total <= e_lo || gbase >= e_hi) {  // no entry of this part here (uniform)
+      gbase += total;
+      continue;
+    }
     for (int base = 0; base < total; base += kWideCap) {
       // Fill: lane t of wave w copies slots s = s_lo + w, s_lo + w + kWideWaves, ...
-      // A spilled tile (count > C) is read by wave 0: its active units in
-      // ascending order, the s-th one going to slot s.
       const int s_lo = max(0, base - off);
       const int s_hi = min(c, base + kWideCap - off);
       if (c <= C) {
@@ -225,25 +250,39 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
           s_j[off + s - base] = t * a.T + (static_cast<int>(a.idx[slot0 + s]) & tmask);
           s_h[off + s - base] = a.vals[slot0 + s];
         }
-      } else if (w == 0 && s_lo < s_hi) {
-        const float* seg = a.spill + (static_cast<size_t>(row) * nT + t) * a.T;
+      }
+      // Spilled tiles (count > C; only when a spill is given): the i-th one of
+      // this group goes to wave i mod kWideWaves, which reads its T z values
+      // 64 at a time; a ballot ranks the active units in ascending order and
+      // the s-th one goes to slot s.
+      uint64_t spilled = __ballot(t < nT && c > C);
+      for (int i = 0; spilled != 0; ++i, spilled &= spilled - 1) {
+        if (i % kWideWaves != w) continue;  // uniform
+        const int tl = __builtin_ctzll(spilled);
+        const int ct = __builtin_amdgcn_readlane(c, tl), ot = __builtin_amdgcn_readlane(off, tl);
+        const int lo_t = max(0, base - ot), hi_t = min(ct, base + kWideCap - ot);
+        if (lo_t >= hi_t) continue;
+        const int tt = t0 + tl;
+        const float* seg = a.spill + (static_cast<size_t>(row) * nT + tt) * a.T;
         int k = 0;
-        for (int u = 0; u < a.T && k < s_hi; ++u) {
-          const float z = seg[u];
-          if (z > 0.f) {
-            if (k >= s_lo) {
-              s_j[off + k - base] = t * a.T + u;
-              s_h[off + k - base] = z;
-            }
-            ++k;
+        for (int u0 = 0; u0 < a.T; u0 += 64) {  // T is 64 or 128
+          const float z = seg[u0 + lane];
+          const uint64_t b = __ballot(z > 0.f);
+          const int sl = k + static_cast<int>(mask_rank(b));
+          if (z > 0.f && sl >= lo_t && sl < hi_t) {
+            s_j[ot + sl - base] = tt * a.T + u0 + lane;
+            s_h[ot + sl - base] = z;
           }
+          k += __popcll(b);
         }
       }
       __syncthreads();
-      const int n = min(kWideCap, total - base);
+      // this round's entries that belong to this part: [lo, n)
+      const int lo = max(0, e_lo - gbase - base);
+      const int n = min(min(kWideCap, total - base), e_hi - gbase - base);
 
       // Up: chunks of UP entries round-robin over the waves.
-      for (int e0 = w * UP; e0 < n; e0 += kWideWaves * UP) {
+      for (int e0 = lo + w * UP; e0 < n; e0 += kWideWaves * UP) {
         // lane u holds entry e0 + u (the last entry for lanes past the list)
         const int jv = s_j[min(e0 + min(lane, UP - 1), n - 1)];
         const float gv = s_h[min(e0 + min(lane, UP - 1), n - 1)];
@@ -269,7 +308,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
       __syncthreads();
 
       // Down: the whole list in order, DN entries' loads at a time.
-      for (int e0 = 0; e0 < n; e0 += DN) {
+      for (int e0 = lo; e0 < n; e0 += DN) {
         const int jv = s_j[min(e0 + min(lane, DN - 1), n - 1)];
         const float hv = s_h[min(e0 + min(lane, DN - 1), n - 1)];
         u32x2_t wd[DN][NQ];
@@ -301,13 +340,50 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
       }
       __syncthreads();  // the list is refilled next round
     }
+    gbase += total;
   }
 
   float* yr = a.y + static_cast<size_t>(row) * a.d;
+  if (P == 1) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = (i * kWideWaves + w) * 64 + lane;
+      if (q < quads) *reinterpret_cast<float4*>(yr + 4 * q) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+    return;
+  }
+  // Partial y row of this part; the last part to arrive (a per-row counter,
+  // reset by it) adds parts 0 .. P-1 in order.
+  float* prow = a.part + (static_cast<size_t>(part_k) * a.M + row) * a.d;
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const int q = (i * kWideWaves + w) * 64 + lane;
-    if (q < quads) *reinterpret_cast<float4*>(yr + 4 * q) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    if (q < quads) *reinterpret_cast<float4*>(prow + 4 * q) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+  __threadfence();  // release this part
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = atomicAdd(&a.counters[row], 1u);
+    s_last = done == static_cast<uint32_t>(P - 1);
+    if (s_last) __hip_atomic_store(&a.counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // acquire the other parts
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int q = (i * kWideWaves + w) * 64 + lane;
+    if (q < quads) {
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < P; ++k) {
+        const float4 v = reinterpret_cast<const float4*>(a.part + (static_cast<size_t>(k) * a.M + row) * a.d)[q];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+      }
+      *reinterpret_cast<float4*>(yr + 4 * q) = sum;
+    }
   }
 }
 
@@ -329,7 +405,8 @@ hipError_t launch_vec(const FusedArgs& a, hipStream_t s) {
     // entries per up round per wave / per down round: as deep as registers allow
     constexpr int kUp = NCH <= 2 ? 8 : (NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1));
     constexpr int kDn = kNQ == 1 ? 64 : (kNQ == 2 ? 24 : 8);
-    fused_updown_wide_kernel<VEC, NCH, kUp, kNQ, kDn><<<dim3(a.M), dim3(64 * kWideWaves), 0, s>>>(a);
+    fused_updown_wide_kernel<VEC, NCH, kUp, kNQ, kDn>
+        <<<dim3(a.M * std::max(a.splits, 1)), dim3(64 * kWideWaves), 0, s>>>(a);
     return hipGetLastError();
   }
   const dim3 grid((a.M + kRowsPerWG - 1) / kRowsPerWG), block(64 * kRowsPerWG);

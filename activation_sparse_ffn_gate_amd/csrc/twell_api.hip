@@ -158,6 +158,25 @@ int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, 
   return hip_status(twell::launch_gate_pack(a, s));
 }
 
+twell::FusedArgs fused_args(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
+                            int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y) {
+  twell::FusedArgs a;
+  a.x = x;
+  a.WuT = WuT;
+  a.Wd = Wd;
+  a.vals = in->vals;
+  a.idx = in->idx;
+  a.counts = in->counts;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.y = y;
+  a.spill = nullptr;
+  return a;
+}
+
 int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
                int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s,
                const float* spill = nullptr) {
@@ -430,10 +449,17 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     // Few rows (the small-batch gate's range): it spills the z of every overflowing
     // (row, tile) into the fallback's region, and the fused kernel (a
     // workgroup per row) does overflow rows from it: two launches in all.
+    // Long rows are cut over several workgroups (partial rows in the split-K
+    // region, one arrival counter per row among the fallback's, both idle here).
     float* spill = at<float>(workspace, L.h_hi);  // M F floats: the region holds 2 M F bf16
     st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill);
     if (st != TWELL_OK) return st;
-    return fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s, spill);
+    twell::FusedArgs a = fused_args(x, WuT, Wd, &p, M, d, F, T, C, y);
+    a.spill = spill;
+    a.splits = int(std::min<int64_t>(16, std::max<int64_t>(1, 512 / M)));  // splits M <= 512 rows of d floats
+    a.part = at<float>(workspace, L.split);
+    a.counters = fallback_counters(ctrl, M);
+    return hip_status(twell::launch_fused_updown(a, s));
   }
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;

@@ -40,6 +40,11 @@ struct FusedArgs {
   int M, d, F, T, C;
   float* y;
   const float* spill;  // nullable: rows with a tile count > C are done from it (else left to the fallback)
+  // Workgroup-per-row form: long rows cut into up to `splits` parts, partial y
+  // rows in part [splits, M, d], per-row arrival counters (zero, left zero).
+  int splits = 1;
+  float* part = nullptr;
+  uint32_t* counters = nullptr;
 };
 
 // Dense gated FFN over a list of rows (all rows, or the overflow rows).

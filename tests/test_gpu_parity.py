@@ -123,8 +123,9 @@ def test_components_compose(name):
     """gate_pack + (sliced or fused) up/down + dense_fallback == ffn_forward,
     bit for bit; the up/down kernels leave overflow rows alone; packed_view
     shows the packing. Up to 256 rows the forward does overflow rows from the
-    gate's spilled z instead of the fallback: there the rows that fit are
-    compared bit for bit and the overflow rows against the definition."""
+    gate's spilled z instead of the fallback, and cuts rows of more than 384
+    units over several workgroups (another sum order): there the other rows
+    are compared bit for bit and these against the definition."""
     inp, _, _, Y = small_case(name)
     w = inp.workload
     x, Wg, WuT, Wd = dev(inp)
@@ -146,10 +147,13 @@ def test_components_compose(name):
     if w.M > 256:
         assert np.array_equal(yc.view(np.uint32), yf.view(np.uint32))
     else:
-        assert np.array_equal(yc[fit].view(np.uint32), yf[fit].view(np.uint32))
-        if len(ovf):
-            rel, _ = check_y(yf[ovf], Y[ovf])
-            print(f"{name}: {len(ovf)} overflow rows from the spill, rel L2 {rel:.2e}")
+        total = g["counts"].astype(np.int64).sum(axis=1)
+        same = np.setdiff1d(fit, np.flatnonzero(total > 384))
+        other = np.union1d(ovf, np.flatnonzero(total > 384))
+        assert np.array_equal(yc[same].view(np.uint32), yf[same].view(np.uint32))
+        if len(other):
+            rel, _ = check_y(yf[other], Y[other])
+            print(f"{name}: {len(ovf)} overflow rows from the spill, {len(other)} rows spilled or cut, rel L2 {rel:.2e}")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
