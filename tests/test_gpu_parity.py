@@ -55,6 +55,9 @@ SMALL = {
     "few_rows_d768": scaled(WORKLOADS["ffn1p5b"], M=5, d=768, F=2048),
     "few_rows_d2560": scaled(WORKLOADS["ffn2b_zipf"], M=7, d=2560, F=2560),
     "few_rows_dense30": scaled(WORKLOADS["sweep_p11pct"], M=9, d=512, F=8192, T=64, C=64, mean_nnz=2458.0),
+    # ~490 units a row with C = 8: rows cut over several workgroups that also
+    # hold spilled (overflowing) tiles
+    "few_rows_cut_spill": scaled(WORKLOADS["sweep_p3pct"], M=24, d=512, F=16384, C=8),
     # the headline's d = 2048 through the small-batch forward and the training path
     "d2048_small": scaled(WORKLOADS["ffn1p5b"], M=200, d=2048, F=1024, mean_nnz=24.0),
 }
