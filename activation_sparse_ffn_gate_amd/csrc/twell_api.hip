@@ -178,24 +178,9 @@ twell::FusedArgs fused_args(const uint16_t* x, const uint16_t* WuT, const uint16
 }
 
 int fused_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, const twell_packed* in,
-               int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s,
-               const float* spill = nullptr) {
+               int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, hipStream_t s) {
   if (M == 0) return TWELL_OK;
-  twell::FusedArgs a;
-  a.x = x;
-  a.WuT = WuT;
-  a.Wd = Wd;
-  a.vals = in->vals;
-  a.idx = in->idx;
-  a.counts = in->counts;
-  a.M = int(M);
-  a.d = int(d);
-  a.F = int(F);
-  a.T = T;
-  a.C = C;
-  a.y = y;
-  a.spill = spill;
-  return hip_status(twell::launch_fused_updown(a, s));
+  return hip_status(twell::launch_fused_updown(fused_args(x, WuT, Wd, in, M, d, F, T, C, y), s));
 }
 
 // `region` is the sliced kernels' workspace region (twell::sliced_layout).

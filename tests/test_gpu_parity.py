@@ -521,3 +521,37 @@ def test_backward_full_size(name):
                                                   inp.Wd[units], dy_bits)
     rels = [check_y(got[units], want)[0] for got, want in ((dWg, gWg), (dWu, gWu), (dWd, gWd))]
     print(f"[full-bwd] {name}: reserve rows {n_res}, dx rel L2 {rel:.2e}, dW rel L2 {max(rels):.2e}")
+
+
+def test_training_edge_cases():
+    """M = 0 (weight gradients all zero, nothing else touched), one row, a
+    batch with no active unit, and R = 0 with every row in blocks."""
+    w = SMALL["few_rows_d768"]
+    inp = make_inputs(w)
+    x, Wg, WuT, Wd = dev(inp)
+    dy_bits = make_upstream_grad(w)
+    dy = to_device(dy_bits, DEV)
+    # M = 0
+    p0 = tw.gate_pack(x[:0], Wg, w.T, w.T)
+    hy0 = tw.hybrid_pack(p0, w.F, 8, 0)
+    assert int(hy0.n_res.item()) == 0
+    g0 = tw.ffn_backward(x[:0], Wg, WuT, Wd, dy[:0], hy0)
+    for t in g0[1:]:
+        assert torch.count_nonzero(t).item() == 0
+    # one row, K large enough for every row (R = 0)
+    z = torch.empty((1, w.F), dtype=torch.float32, device=DEV)
+    p1 = tw.gate_pack(x[:1].contiguous(), Wg, w.T, w.T, z_debug=z)
+    hy1 = tw.hybrid_pack(p1, w.F, w.F, 0)
+    got = [t.cpu().numpy() for t in tw.ffn_backward(x[:1].contiguous(), Wg, WuT, Wd, dy[:1].contiguous(), hy1)]
+    want = O.ffn_backward_from_hybrid(O.hybrid_pack(z.cpu().numpy(), w.F), inp.x[:1], inp.Wg, inp.WuT, inp.Wd,
+                                      dy_bits[:1])
+    for g, r in zip(got, want):
+        check_y(g, r)
+    # no active unit at all: every gradient is exactly zero
+    Wneg = (-Wg.float().abs()).to(torch.bfloat16).contiguous()
+    xpos = x.float().abs().to(torch.bfloat16).contiguous()
+    pz = tw.gate_pack(xpos, Wneg, w.T, w.T)
+    hyz = tw.hybrid_pack(pz, w.F, 8, w.M)
+    assert int(hyz.count.sum().item()) == 0
+    for t in tw.ffn_backward(xpos, Wneg, WuT, Wd, dy, hyz):
+        assert torch.count_nonzero(t).item() == 0
