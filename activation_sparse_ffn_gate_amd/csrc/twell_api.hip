@@ -98,6 +98,13 @@ int check_tc(int64_t F, int32_t T, int32_t C) {
   return TWELL_OK;
 }
 
+// The gate kernels address x, Wg and the packed values with 32-bit byte offsets.
+int check_gate_offsets(int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
+  const int64_t lim = int64_t(1) << 31;
+  if (M * d * 2 >= lim || F * d * 2 >= lim || M * (F / T) * int64_t(C) * 4 >= lim) return TWELL_E_UNSUPPORTED;
+  return TWELL_OK;
+}
+
 int check_ws(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C, void* ws, size_t ws_bytes) {
   const Layout L = layout(op, M, F, T, C);
   if (L.total == 0) return TWELL_OK;
@@ -367,6 +374,7 @@ int twell_gate_pack(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d,
   if ((M != 0 && !x) || !Wg || !packed_ok(out, M)) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st != TWELL_OK) return st;
   return gate_pack_impl(x, Wg, M, d, F, T, C, out, z_debug, static_cast<uint32_t*>(ctrl),
@@ -423,6 +431,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
@@ -477,6 +486,7 @@ int twell_column_activity(const uint16_t* x, const uint16_t* Wg, int64_t M, int6
   if ((M != 0 && !x) || !Wg || !active_bits) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
   if (st == TWELL_OK) st = check_ws(TWELL_OP_COLUMN_ACTIVITY, M, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;

@@ -25,7 +25,10 @@
  *    before anything is enqueued; execution errors surface at the caller's
  *    stream synchronisation. No exception crosses the ABI.
  *  - Shape limits: M >= 0 and M < 2^31; d % 256 == 0 and 256 <= d <= 8192;
- *    F > 0 with F % T == 0; T in {64, 128}; 1 <= C <= T.
+ *    F > 0 with F % T == 0; T in {64, 128}; 1 <= C <= T. Calls that run the
+ *    gate (twell_gate_pack, twell_column_activity, twell_ffn_forward) also
+ *    need M d 2, F d 2 and M (F / T) C 4 below 2^31 bytes (32-bit offsets);
+ *    larger shapes return TWELL_E_UNSUPPORTED (split the batch).
  *  - Workspace: a caller-owned device scratch buffer of at least
  *    twell_workspace_bytes(op, ...) bytes, 256-byte aligned, contents
  *    irrelevant. One workspace must not be used by two calls that may run

@@ -234,3 +234,19 @@ def test_backward_validation():
     assert fb(*bad_d, FAKE, ws, None) == E_UNSUP
     no_dx = ok[:11] + [None] + ok[12:]
     assert fb(*no_dx, FAKE, ws, None) == E_ARG
+
+
+def test_gate_offset_limits():
+    """Shapes whose x, Wg or packed values pass 2^31 bytes are refused before
+    anything is enqueued (the gate kernels use 32-bit offsets)."""
+    L = tw.lib()
+    pk = _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    g = tw.ctrl_bytes(1 << 20)
+    # x: 2^20 rows of d = 1024 is 2^31 bytes
+    assert L.twell_gate_pack(FAKE, FAKE, 1 << 20, 1024, 1024, 128, 16, ctypes.byref(pk), None, FAKE, g, None) == E_UNSUP
+    # Wg: 2^20 units of d = 1024
+    assert L.twell_gate_pack(FAKE, FAKE, 64, 1024, 1 << 20, 128, 16, ctypes.byref(pk), None, FAKE,
+                             tw.ctrl_bytes(64), None) == E_UNSUP
+    # packed values: M (F / T) C 4 = 2^31 with M = 2^17, F = 8192, T = 128, C = 64
+    assert L.twell_gate_pack(FAKE, FAKE, 1 << 17, 256, 8192, 128, 64, ctypes.byref(pk), None, FAKE,
+                             tw.ctrl_bytes(1 << 17), None) == E_UNSUP
