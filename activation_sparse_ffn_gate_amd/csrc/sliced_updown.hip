@@ -42,7 +42,12 @@
 namespace twell {
 namespace {
 
-constexpr int kRowsPerWG = 4;      // one wave per (row, slice)
+// One wave per (row, slice), one wave per workgroup (no wave of these kernels
+// waits for another). Measured against 2, 4 and 8 waves a workgroup,
+// single-wave workgroups were the fastest: 93 against 99 us for the pair at
+// M = 4096, d = 2048, F = 8192, and 373 against 402 us at M = 16384,
+// d = 2560, F = 10240.
+constexpr int kRowsPerWG = 1;
 constexpr int kListCap = 256;       // stored units staged per wave per round
 constexpr int kListPad = 64;        // staged lists are padded (unit 0, value 0) to a whole step
 constexpr int kCountGroups = 2;     // rows of up to 128 tiles keep their counts in registers
@@ -134,7 +139,7 @@ __device__ __forceinline__ int stage_row(const SlicedArgs& a, int row, const int
 }
 
 template <int L, int V, int U>
-__global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
+__global__ __launch_bounds__(64 * kRowsPerWG) void sliced_up_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
   __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
   __shared__ float s_g[kRowsPerWG][kListCap + kListPad];
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void sliced_up_kernel(SlicedArgs a) {
 // L > 32 (one group, lanes >= L idle) avoids the cross-group sum for the
 // slice widths that are not a power-of-two number of pieces.
 template <int L, int V, int U>
-__global__ __launch_bounds__(256) void sliced_down_kernel(SlicedArgs a) {
+__global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
   __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
   __shared__ float s_h[kRowsPerWG][kListCap + kListPad];
