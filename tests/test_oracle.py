@@ -6,7 +6,8 @@ every planted mistake must make at least one pin fail.
 
 What pins what:
 * decode_bf16            IEEE-754 bit patterns with known values.
-* dense_gated_ffn        a hand-worked example with closed-form output; exact
+* dense_gated_ffn        a hand-worked example with closed-form output (inputs,
+                         values and derivation in tests/golden/); exact
                          integer brute force (Python ints, no floating point);
                          the identity ReLU(z) - ReLU(-z) = z, which turns the
                          difference of two FFN outputs into a bilinear form
@@ -39,6 +40,8 @@ What pins what:
                          full weights (dropped terms are exact zeros).
 """
 
+import json
+import os
 import types
 
 import numpy as np
@@ -72,28 +75,18 @@ def rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
-# The hand-worked example. Derivation (every number is exact):
-#   x row 0 = [1, 2, 0, -1], row 1 = [1, 0, 1, 1]
-#   z = x Wg^T:  row 0 = [-5, 2, -2, -9]   row 1 = [-5, 0, 1, -9]
-#   u = x Wu^T:  row 0 = [ 2, 5,  1,  1]   row 1 = [ 3, 3, 1,  1]
-#   h = ReLU(z) * u: row 0 = [0, 10, 0, 0] row 1 = [0, 0, 1, 0]   (z = 0 is off)
-#   y = h Wd:    row 0 = 10 * Wd[1] = [10, -10, 20, 5]
-#                row 1 =  1 * Wd[2] = [ 4,   0, -2, 1]
-#   TwELL with T = 2, C = 1: tile 0 holds units {0, 1}, tile 1 holds {2, 3}.
-#     row 0: tile 0 -> count 1, local index 1, value 2; tile 1 -> count 0
-#     row 1: tile 0 -> count 0 (its z = 0 is not active); tile 1 -> count 1,
-#            local index 0 (unit 2 is the first column of tile 1), value 1
-HAND = dict(
-    x=[[1, 2, 0, -1], [1, 0, 1, 1]],
-    Wg=[[-5, 0, 0, 0], [0, 1, 0, 0], [-1, 0, 1, 1], [-9, 0, 0, 0]],
-    WuT=[[1, 1, 1, 1], [3, 1, 0, 0], [0, 0, 2, -1], [1, 0, 0, 0]],
-    Wd=[[100, 100, 100, 100], [1, -1, 2, 0.5], [4, 0, -2, 1], [-7, 7, -7, 7]],
-    z=[[-5, 2, -2, -9], [-5, 0, 1, -9]],
-    y=[[10, -10, 20, 5], [4, 0, -2, 1]],
-    counts=[[1, 0], [0, 1]],
-    idx0=[[1, None], [None, 0]],
-    val0=[[2.0, None], [None, 1.0]],
-)
+# The hand-worked examples (inputs, expected values, derivation and the
+# passages they follow) are stored under tests/golden/.
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+HAND = golden("forward_hand_example.json")
+HAND_BWD = golden("backward_hand_example.json")
 
 
 # --------------------------------------------------------------------- pins
@@ -112,14 +105,14 @@ def pin_hand_example(o):
     assert np.array_equal(Z, np.array(HAND["z"], dtype=np.float64))
     y = o.dense_gated_ffn(h["x"], h["Wg"], h["WuT"], h["Wd"])
     assert np.array_equal(y, np.array(HAND["y"], dtype=np.float64))
-    p = o.pack_twell(Z.astype(np.float32), T=2, C=1)
+    p = o.pack_twell(Z.astype(np.float32), T=HAND["T"], C=HAND["C"])
     assert p.counts.tolist() == HAND["counts"]
     for r in range(2):
         for t in range(2):
             if HAND["idx0"][r][t] is not None:
                 assert int(p.idx[r, t, 0]) == HAND["idx0"][r][t]
                 assert float(p.vals[r, t, 0]) == HAND["val0"][r][t]
-    assert len(p.ovf) == 0
+    assert sorted(int(r) for r in p.ovf) == HAND["overflow_rows"]
     G = o.unpack_twell(p, 4)
     assert np.array_equal(G, np.maximum(np.array(HAND["z"], dtype=np.float32), 0))
     assert np.array_equal(o.ffn_from_twell(p, h["x"], h["Wg"], h["WuT"], h["Wd"]), y)
@@ -360,18 +353,12 @@ def pin_compaction_keeps_ffn(o):
 
 
 def pin_backward_hand_example(o):
-    # x = [1, 2]; z = [1, -2]; g = [1, 0]; u = [3, 2]; h = [3, 0]; dy = [1, 1]
-    # dH = [1, 1]; dZ = [3, 0]; dU = [1, 0]; dx = 3 [1, 0] + 1 [1, 1] = [4, 1]
-    x = bf([[1.0, 2.0]])
-    Wg = bf([[1.0, 0.0], [0.0, -1.0]])
-    WuT = bf([[1.0, 1.0], [2.0, 0.0]])
-    Wd = bf([[1.0, 0.0], [0.0, 1.0]])
-    dy = bf([[1.0, 1.0]])
-    dx, dWg, dWu, dWd = o.ffn_backward(x, Wg, WuT, Wd, dy)
-    assert dx.tolist() == [[4.0, 1.0]]
-    assert dWg.tolist() == [[3.0, 6.0], [0.0, 0.0]]
-    assert dWu.tolist() == [[1.0, 2.0], [0.0, 0.0]]
-    assert dWd.tolist() == [[3.0, 3.0], [0.0, 0.0]]
+    h = {k: bf(HAND_BWD[k]) for k in ("x", "Wg", "WuT", "Wd", "dy")}
+    dx, dWg, dWu, dWd = o.ffn_backward(h["x"], h["Wg"], h["WuT"], h["Wd"], h["dy"])
+    assert dx.tolist() == HAND_BWD["dx"]
+    assert dWg.tolist() == HAND_BWD["dWg"]
+    assert dWu.tolist() == HAND_BWD["dWu"]
+    assert dWd.tolist() == HAND_BWD["dWd"]
 
 
 def pin_backward_finite_difference(o):
