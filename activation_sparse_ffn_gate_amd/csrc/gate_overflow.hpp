@@ -1,8 +1,9 @@
 // Overflow-row set of the gate kernels (both tile shapes).
 //
 // A row overflows when one of its (row, tile) counts exceeds C; its rows go
-// to the dense fallback (TwELL hybrid format: Tencent Cloud article, section 3;
-// pulsen.vercel.app article, paragraph on overflow rows). The set is built
+// to the dense fallback (rows that do not fit the sparse block fall back to a
+// dense buffer: Telegram post on TwELL at tgviewer.app, part "Обучение";
+// Tencent Cloud article, section 3). The set is built
 // with device-scope atomics in the caller's control block, which is zero
 // before every call and left zero after it:
 //   word 0 (64-bit): low half = rows appended so far, high half = workgroups

@@ -102,6 +102,8 @@ def parse():
     ap.add_argument("--record-traffic", metavar="DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc outputs under DIR (no GPU needed)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the density sweep")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the heavy-tailed and 2B-like layers' forward legs")
     ap.add_argument("--compact", action="store_true",
                     help="with --only: run on the layer with its never-active units dropped")
     ap.add_argument("--sweep-steps", type=int, default=10)
@@ -369,6 +371,188 @@ def dead_unit_compaction(dev, name, steps, warmup):
     return out
 
 
+def load_traffic(workload):
+    """HBM-side bytes per launch recorded from rocprofv3 counters for this
+    workload, or {} when the kernel sources changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256") != sources_hash():
+        return {}
+    return rec.get("workloads", {}).get(workload, {})
+
+
+def updown_bytes(counts, w):
+    """Algorithmic bytes of one up/down pass over a packing (counts [M, F/T]).
+
+    G (gathered): every stored unit of a row that fits reads one WuT and one
+    Wd row (4 d bytes); U (distinct): each unit's two rows are read once
+    however many rows store it. Both add, per fitting row, x (2 d) and y
+    (4 d), and the packing read (2 bytes per count, 5 per stored slot)."""
+    nT = w.F // w.T
+    fit = counts.max(axis=1) <= w.C
+    nnz_fit = int(counts[fit].sum())
+    io = float(fit.sum()) * 6.0 * w.d + w.M * 2.0 * nT + nnz_fit * 5.0
+    return dict(nnz_fit=nnz_fit, fit_rows=int(fit.sum()), G=nnz_fit * 4.0 * w.d + io, io=io)
+
+
+def distinct_units(view, w):
+    """Units stored by at least one fitting row of a device packing."""
+    import torch
+
+    nT = w.F // w.T
+    counts = view.counts.view(torch.int16).to(torch.int32) & 0xFFFF
+    fit = (counts.max(dim=1).values <= w.C)
+    used = torch.arange(w.C, device=counts.device)[None, None, :] < torch.clamp(counts, max=w.C)[:, :, None]
+    used &= fit[:, None, None]
+    unit = view.idx.to(torch.int64) + (torch.arange(nT, device=counts.device) * w.T)[None, :, None]
+    mark = torch.zeros(w.F, dtype=torch.bool, device=counts.device)
+    mark[unit[used]] = True
+    return int(mark.sum().item())
+
+
+def kernel_legs(dev, w, tensors, k_steps, workload, bufs=None):
+    """Each component of the forward timed alone with HIP events on its launch
+    stream (k_steps back-to-back launches), the dense baselines, and the
+    roofline of the slower of the gate and the up/down step."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+
+    x, Wg, WuT, Wd = tensors
+    b = bufs or {}
+
+    def buf(key, make):  # the caller's buffer if given, else a new one
+        return b[key] if b.get(key) is not None else make()
+
+    y = buf("y", lambda: torch.empty((w.M, w.d), dtype=torch.float32, device=dev))
+    ctrl_gate = buf("ctrl_gate", lambda: tw.Workspace(dev, zeroed=True))
+    ws_dense = buf("ws_dense", lambda: tw.Workspace(dev))
+    packed = buf("packed", lambda: tw.Packed.empty(w.M, w.F, w.T, w.C, dev))
+    ws_sliced = buf("ws_sliced", lambda: tw.Workspace(dev))
+    stream = torch.cuda.current_stream(dev)
+    y_dense = torch.empty_like(y)
+
+    gate = lambda: tw.gate_pack(x, Wg, w.T, w.C, out=packed, ctrl=ctrl_gate)  # noqa: E731
+    fused = lambda: tw.fused_updown(x, WuT, Wd, packed, y=y)  # noqa: E731
+    sliced_ok = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, w.M, w.d, w.F, w.T, w.C) > 0
+    sliced = lambda: tw.sliced_updown(x, WuT, Wd, packed, y=y, workspace=ws_sliced)  # noqa: E731
+    fallback = lambda: tw.dense_fallback(x, Wg, WuT, Wd, packed, y, workspace=ws_dense)  # noqa: E731
+    dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y_dense, workspace=ws_dense)  # noqa: E731
+    dense_tl = dense_torch(x, Wg, WuT, Wd)
+
+    gate()
+    torch.cuda.synchronize()
+    counts = packed.counts.cpu().numpy().view(np.uint16).astype(np.int64)
+    n_ovf = int(packed.n_ovf.item())
+    nnz_all = int(counts.sum())
+    ub = updown_bytes(counts, w)
+    U = distinct_units(packed, w) * 4.0 * w.d + ub["io"]
+    for fn in [gate, fused, fallback, dense, dense_tl] + ([sliced] if sliced_ok else []):
+        fn()
+    torch.cuda.synchronize()
+    t_gate = time_loop(gate, k_steps, stream)
+    t_fused = time_loop(fused, k_steps, stream)
+    t_sliced = time_loop(sliced, k_steps, stream) if sliced_ok else None
+    t_fb = time_loop(fallback, k_steps, stream)
+    t_dense = time_loop(dense, k_steps, stream)
+    t_dense_tl = time_loop(dense_tl, k_steps, stream)
+    # the up/down form twell_ffn_forward runs above 256 rows
+    t_updown = t_sliced if sliced_ok else t_fused
+    updown_name = "sliced_updown" if sliced_ok else "fused_updown"
+
+    gate_flops = 2.0 * w.M * w.d * w.F
+    gate_tflops = gate_flops / (t_gate * 1e-3) / 1e12
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    traffic = load_traffic(workload)
+    hbm = {k: round(v["traffic_bytes"]) for k, v in traffic.items()}
+
+    def hbm_gbs(name, ms):
+        return round(gbs(hbm[name], ms), 1) if name in hbm else None
+
+    if t_updown >= t_gate:
+        roof = {"kernel": updown_name, "bound": "hbm", "achieved": round(gbs(U, t_updown), 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs(U, t_updown) / PEAK_HBM_GBS, 4),
+                "traffic": hbm.get(updown_name), "bytes": "distinct (U)"}
+    else:
+        roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(gate_tflops, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": hbm.get("gate_pack")}
+    legs = {
+        "gate_pack_ms": round(t_gate, 5),
+        "gate_pack_tflops": round(gate_tflops, 1),
+        "gate_pack_mfma_frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4),
+        "gate_pack_hbm_bytes": hbm.get("gate_pack"),
+        "fused_updown_ms": round(t_fused, 5),
+        "sliced_updown_ms": round(t_sliced, 5) if sliced_ok else None,
+        "forward_updown": updown_name,
+        "updown_gathered_bytes": round(ub["G"]),
+        "updown_distinct_bytes": round(U),
+        "fused_updown_gathered_gbs": round(gbs(ub["G"], t_fused), 1),
+        "fused_updown_distinct_gbs": round(gbs(U, t_fused), 1),
+        "fused_updown_distinct_hbm_frac": round(gbs(U, t_fused) / PEAK_HBM_GBS, 4),
+        "fused_updown_hbm_bytes": hbm.get("fused_updown"),
+        "fused_updown_counter_gbs": hbm_gbs("fused_updown", t_fused),
+        "dense_fallback_ms": round(t_fb, 5),
+        "nnz_per_token": round(nnz_all / w.M, 3),
+        "overflow_rows": n_ovf,
+        "traffic_current": bool(traffic),
+    }
+    if sliced_ok:
+        legs.update({
+            "sliced_updown_gathered_gbs": round(gbs(ub["G"], t_sliced), 1),
+            "sliced_updown_distinct_gbs": round(gbs(U, t_sliced), 1),
+            "sliced_updown_distinct_hbm_frac": round(gbs(U, t_sliced) / PEAK_HBM_GBS, 4),
+            "sliced_updown_hbm_bytes": hbm.get("sliced_updown"),
+            "sliced_updown_counter_gbs": hbm_gbs("sliced_updown", t_sliced),
+        })
+    legs["roofline"] = roof
+    legs["dense_baseline"] = {
+        "ms": round(t_dense, 5),
+        "tokens_per_s": round(w.M / (t_dense * 1e-3), 1),
+        "tflops": round(3 * gate_flops / (t_dense * 1e-3) / 1e12, 1),
+        "hipblaslt_ms": round(t_dense_tl, 5),
+        "hipblaslt_tflops": round(3 * gate_flops / (t_dense_tl * 1e-3) / 1e12, 1),
+    }
+    return legs
+
+
+def layer_report(dev, name, k_steps, warmup):
+    """Forward throughput of another full-size layer with its kernel legs."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_gate_amd as tw
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    x, Wg, WuT, Wd = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+                      for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
+    y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
+    ws, ctrl = tw.Workspace(dev), tw.Workspace(dev, zeroed=True)
+    stream = torch.cuda.current_stream(dev)
+    fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)  # noqa: E731
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t_fwd = time_loop(fwd, k_steps, stream)
+    legs = kernel_legs(dev, w, (x, Wg, WuT, Wd), k_steps, name)
+    out = {"workload": name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C,
+           "forward_ms": round(t_fwd, 5), "tokens_per_s": round(w.M / (t_fwd * 1e-3), 1),
+           "roofline": legs.pop("roofline")}
+    dense = legs.pop("dense_baseline")
+    dense["speedup_sparse_vs_dense"] = round(dense["ms"] / t_fwd, 3)
+    dense["speedup_sparse_vs_hipblaslt"] = round(dense["hipblaslt_ms"] / t_fwd, 3)
+    out["kernels"] = legs
+    out["dense_baseline"] = dense
+    del x, Wg, WuT, Wd, y, ws, ctrl
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle, as it stands, on a bounded sample of the same layer's rows."""
     import numpy as np
@@ -389,10 +573,17 @@ def cpu_baseline(inp, budget_s):
         rows_done += len(rows)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(rows_done / dt, 2),
         "unit": "tokens/s",
         "cores": int(threads),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"first {rows_done} of {w.M} tokens of {w.name}: fp64 gate, TwELL pack, "
                   f"fp64 dense FFN and sparse FFN from the packing ({dt:.1f} s)",
@@ -497,55 +688,17 @@ def main():
     value = w.M * args.steps / elapsed
 
     # ------------------------------------------------- per-kernel (HIP events)
-    gate()
-    torch.cuda.synchronize()
-    counts = packed.counts.cpu().numpy().view(np.uint16).astype(np.int64)
-    n_ovf = int(packed.n_ovf.item())
-    fit = counts.max(axis=1) <= w.C
-    nnz_fit = int(counts[fit].sum())
-    nnz_all = int(counts.sum())
     k_steps = max(args.steps, 20)
-    dense_tl = dense_torch(x, Wg, WuT, Wd)
-    legs = [gate, fused, fallback, dense, dense_tl] + ([sliced] if sliced_ok else [])
-    for fn in legs:
-        fn()
-    torch.cuda.synchronize()
-    t_gate = time_loop(gate, k_steps, stream)
-    t_fused = time_loop(fused, k_steps, stream)
-    t_sliced = time_loop(sliced, k_steps, stream) if sliced_ok else None
-    t_fb = time_loop(fallback, k_steps, stream)
-    t_dense = time_loop(dense, k_steps, stream)
-    t_dense_tl = time_loop(dense_tl, k_steps, stream)
+    legs = kernel_legs(dev, w, (x, Wg, WuT, Wd), k_steps, args.workload,
+                       bufs=dict(y=y, ws_fwd=ws_fwd, ctrl_fwd=ctrl_fwd, ctrl_gate=ctrl_gate, ws_dense=ws_dense,
+                                 packed=packed, ws_sliced=ws_sliced))
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     lat = {"warm": latency(fwd, 20), "cold": latency(fwd, 20, flush=flush)}
     del flush
-    # the up/down form twell_ffn_forward runs
-    t_updown = t_sliced if sliced_ok else t_fused
-    updown_name = "sliced_updown" if sliced_ok else "fused_updown"
-
-    nT = w.F // w.T
-    gate_flops = 2.0 * w.M * w.d * w.F
-    # algorithmic bytes of one fused launch: each stored unit gathers one WuT and
-    # one Wd row (2 * 2d bytes); each row reads x (2d), its counts (2 nT) and
-    # stored slots (5 bytes each) and writes y (4d)
-    fused_bytes = nnz_fit * 4.0 * w.d + fit.sum() * (2.0 * w.d + 4.0 * w.d) + w.M * 2.0 * nT + nnz_fit * 5.0
-    gate_tflops = gate_flops / (t_gate * 1e-3) / 1e12
-    fused_gbs = fused_bytes / (t_fused * 1e-3) / 1e9
-    updown_gbs = fused_bytes / (t_updown * 1e-3) / 1e9
-    traffic = None  # HBM-side bytes per launch from the recorded counters, if still current
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-        if rec.get("sources_sha256") == sources_hash():
-            ent = rec.get("workloads", {}).get(args.workload, {})
-            kern = ent.get(updown_name if t_updown >= t_gate else "gate_pack")
-            traffic = round(kern["traffic_bytes"]) if kern else None
-    if t_updown >= t_gate:
-        roof = {"kernel": updown_name, "bound": "hbm", "achieved": round(updown_gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(updown_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(gate_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    roof = legs.pop("roofline")
+    dense = legs.pop("dense_baseline")
+    dense["speedup_sparse_vs_dense"] = round(dense["ms"] / ms_step, 3)
+    dense["speedup_sparse_vs_hipblaslt"] = round(dense["hipblaslt_ms"] / ms_step, 3)
 
     out = {
         "metric": METRIC,
@@ -563,31 +716,15 @@ def main():
         "config": {"workload": w.name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C,
                    "mean_nnz_target": round(w.mean_nnz, 3), "parallelism": "none"},
         "roofline": roof,
-        "kernels": {
-            "gate_pack_ms": round(t_gate, 5),
-            "gate_pack_tflops": round(gate_tflops, 1),
-            "gate_pack_mfma_frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4),
-            "fused_updown_ms": round(t_fused, 5),
-            "fused_updown_gbs": round(fused_gbs, 1),
-            "fused_updown_hbm_frac": round(fused_gbs / PEAK_HBM_GBS, 4),
-            "sliced_updown_ms": round(t_sliced, 5) if sliced_ok else None,
-            "sliced_updown_gbs": round(updown_gbs, 1) if sliced_ok else None,
-            "forward_updown": updown_name,
-            "dense_fallback_ms": round(t_fb, 5),
-            "nnz_per_token": round(nnz_all / w.M, 3),
-            "overflow_rows": n_ovf,
-        },
+        "kernels": legs,
         "latency_forward": lat,
-        "dense_baseline": {
-            "ms": round(t_dense, 5),
-            "tokens_per_s": round(w.M / (t_dense * 1e-3), 1),
-            "tflops": round(3 * gate_flops / (t_dense * 1e-3) / 1e12, 1),
-            "speedup_sparse_vs_dense": round(t_dense / ms_step, 3),
-            "hipblaslt_ms": round(t_dense_tl, 5),
-            "hipblaslt_tflops": round(3 * gate_flops / (t_dense_tl * 1e-3) / 1e12, 1),
-            "speedup_sparse_vs_hipblaslt": round(t_dense_tl / ms_step, 3),
-        },
+        "dense_baseline": dense,
     }
+    del x, Wg, WuT, Wd, y, ws_fwd, ctrl_fwd, ctrl_gate, ws_dense, packed, ws_sliced
+    torch.cuda.empty_cache()
+    if not args.no_layers:  # the other full-size layers: heavy-tailed 1.5B-like and 2B-like
+        out["layers"] = [layer_report(dev, n, k_steps, args.warmup)
+                         for n in ("ffn1p5b_heavytail", "ffn2b_zipf") if n != args.workload]
     if not args.no_sweep:  # HBM holds both layers' buffers easily
         from synth import WORKLOADS as _W
 

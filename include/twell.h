@@ -24,8 +24,9 @@
  *    void*; NULL = the default stream). Errors found on the host are returned
  *    before anything is enqueued; execution errors surface at the caller's
  *    stream synchronisation. No exception crosses the ABI.
- *  - Shape limits: M >= 0 and M < 2^31; d % 256 == 0 and 256 <= d <= 8192;
- *    F > 0 with F % T == 0; T in {64, 128}; 1 <= C <= T. Calls that run the
+ *  - Shape limits: 0 <= M <= 2^30 and 0 < F <= 2^24 (larger values return
+ *    TWELL_E_INVALID_ARG); d % 256 == 0 and 256 <= d <= 8192;
+ *    F % T == 0; T in {64, 128}; 1 <= C <= T. Calls that run the
  *    gate (twell_gate_pack, twell_column_activity, twell_ffn_forward) also
  *    need M d 2, F d 2 and M (F / T) C 4 below 2^31 bytes (32-bit offsets);
  *    larger shapes return TWELL_E_UNSUPPORTED (split the batch).
@@ -144,8 +145,15 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
                          int64_t F, float* y, void* ctrl, size_t ctrl_bytes, void* workspace,
                          size_t ws_bytes, void* stream);
 
-/* The whole sparse forward, on one stream, with the packing kept in the
- * workspace (see twell_packed_view); y [M, d] fp32 is fully written.
+/* The whole sparse forward of the layer: the gate kernel that leaves its
+ * non-zeros in TwELL, then the kernel that does the up and down projections
+ * from that packing without a dense hidden matrix (the two inference kernels:
+ * tgviewer.app Telegram post, part "Инференс"; aimodeling.com summary,
+ * paragraph 3; the gate epilogue feeding a fused up/down pipeline: Tencent
+ * Cloud article, section 2), plus the dense path for rows that overflow the
+ * packing (Telegram post, part "Обучение"; Tencent Cloud article, section 3).
+ * One stream, no host synchronisation, the packing kept in the workspace (see
+ * twell_packed_view); y [M, d] fp32 is fully written.
  * Above 256 rows: twell_gate_pack, then twell_sliced_updown (twell_fused_updown
  * for the d that the sliced form does not support), then twell_dense_fallback.
  * Up to 256 rows: the gate also keeps every z of each (row, tile) whose count

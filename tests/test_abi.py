@@ -250,3 +250,26 @@ def test_gate_offset_limits():
     # packed values: M (F / T) C 4 = 2^31 with M = 2^17, F = 8192, T = 128, C = 64
     assert L.twell_gate_pack(FAKE, FAKE, 1 << 17, 256, 8192, 128, 64, ctypes.byref(pk), None, FAKE,
                              tw.ctrl_bytes(1 << 17), None) == E_UNSUP
+
+
+def test_row_and_unit_limits():
+    """The documented limits: M <= 2^30 and F <= 2^24 are accepted by the
+    sizing calls, one past either is TWELL_E_INVALID_ARG (0 from the sizing
+    calls)."""
+    L = tw.lib()
+    M_max, F_max = 1 << 30, 1 << 24
+    assert tw.ctrl_bytes(M_max) > 0 and tw.ctrl_bytes(M_max + 1) == 0
+    assert tw.workspace_bytes(tw.OP_DENSE_FFN, 64, 256, F_max) > 0
+    assert tw.workspace_bytes(tw.OP_DENSE_FFN, 64, 256, F_max + 64) == 0
+    assert tw.workspace_bytes(tw.OP_FFN_FORWARD, M_max, 256, 1024, 64, 8) > 0
+    assert tw.workspace_bytes(tw.OP_FFN_FORWARD, M_max + 1, 256, 1024, 64, 8) == 0
+    pk = _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    g = tw.ctrl_bytes(64)
+    assert L.twell_gate_pack(FAKE, FAKE, M_max + 1, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE, g,
+                             None) == E_ARG
+    assert L.twell_gate_pack(FAKE, FAKE, 64, 256, F_max + 128, 128, 8, ctypes.byref(pk), None, FAKE, g,
+                             None) == E_ARG
+    # at the limits themselves the gate's 32-bit offsets decide (not the row/unit limit)
+    assert L.twell_gate_pack(FAKE, FAKE, M_max, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE,
+                             tw.ctrl_bytes(M_max), None) == E_UNSUP
+    assert L.twell_gate_pack(FAKE, FAKE, 64, 256, F_max, 128, 8, ctypes.byref(pk), None, FAKE, g, None) == E_UNSUP

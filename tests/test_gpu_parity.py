@@ -2,8 +2,8 @@
 
 Oracle-sized cases span several workgroup tiles and ragged tails; full-size
 cases run the exact launch configuration bench.py times (twell_ffn_forward on
-the full workload) and compare sampled rows, plus the whole packing in the
-bit-exact mode. All inputs come from the seeded generator.
+the full workload) and compare the whole layer: packing bits, active sets and
+every row of y. All inputs come from the seeded generator.
 """
 
 from __future__ import annotations
@@ -439,9 +439,17 @@ def test_deterministic_and_control_block_reset():
 
 
 # ------------------------------------------------------------------ full sizes
+def _chunked(fn, M, step=2048):
+    return np.concatenate([fn(np.arange(s, min(s + step, M))) for s in range(0, M, step)])
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size(name):
-    """The bench configuration (twell_ffn_forward) at the full workload size."""
+    """The bench configuration (twell_ffn_forward) at the full workload size,
+    checked over the whole layer: the forward's own packing and the bit-exact
+    mode's packing both equal the oracle's packing of the bit-exact mode's z,
+    every active set against the fp64 pre-activations, and every row of y
+    against the fp64 definition."""
     inp = make_inputs(WORKLOADS[name])
     w = inp.workload
     print(f"[full] {name} M={w.M} d={w.d} F={w.F} T={w.T} C={w.C}", flush=True)
@@ -451,33 +459,35 @@ def test_full_size(name):
     yh = y.cpu().numpy()
     assert np.isfinite(yh).all(), "some row of y was not written"
 
-    # bit-exact packing of the whole layer against the oracle fed the GPU's z
+    # bit-exact packing of the whole layer: the bit-exact mode's z packed by the
+    # oracle, against that mode's packing and against the forward's own (the
+    # gate instance the forward runs computes the same z)
     z = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV)
     dbg = host_packing(tw.gate_pack(x, Wg, w.T, w.C, z_debug=z))
     zh = z.cpu().numpy()
     del z
-    check_packing_bitexact(dbg, O.pack_twell(zh, w.T, w.C))
-    assert np.array_equal(dbg["counts"], view["counts"]) and np.array_equal(dbg["ovf"], view["ovf"])
+    ref = O.pack_twell(zh, w.T, w.C)
     del zh
+    check_packing_bitexact(dbg, ref)
+    check_packing_bitexact(view, ref)
+    del ref
 
-    # sampled rows: active sets and y against the fp64 definition
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([rng.choice(w.M, min(96, w.M), replace=False), view["ovf"][:32]]))
-    rms = np.sqrt(sum(np.square(O.gate_preactivations(inp.x, inp.Wg, rows=np.arange(s, min(s + 2048, w.M)))).sum(axis=0)
-                      for s in range(0, w.M, 2048)) / w.M)
-    Zs = O.gate_preactivations(inp.x, inp.Wg, rows=rows)
-    check_active_set(view, Zs, rms, w.T, w.C, rows=rows)
-    xs = inp.x[rows]
-    Ys = O.ffn_from_active_set(xs, inp.WuT, inp.Wd, Zs)
-    rel, mx = check_y(yh[rows], Ys)
-    print(f"[full] {name}: overflow rows {view['n_ovf']}, sampled rel L2 {rel:.2e}, max abs {mx:.2e}")
+    # whole layer: active sets and y against the fp64 definition
+    Z = _chunked(lambda r: O.gate_preactivations(inp.x, inp.Wg, rows=r), w.M)
+    rms = O.column_rms(Z)
+    check_active_set(view, Z, rms, w.T, w.C)
+    del Z
+    Y = _chunked(lambda r: O.dense_gated_ffn(inp.x, inp.Wg, inp.WuT, inp.Wd, rows=r), w.M)
+    rel, mx = check_y(yh, Y)
+    print(f"[full] {name}: overflow rows {view['n_ovf']}, whole-tensor rel L2 {rel:.2e}, max abs {mx:.2e}",
+          flush=True)
 
-    # the single-kernel up/down form on the same packing, on the same sampled rows
+    # the single-kernel up/down form on the same packing, completed by the fallback
     p = tw.gate_pack(x, Wg, w.T, w.C)
     yf = tw.fused_updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
     tw.dense_fallback(x, Wg, WuT, Wd, p, yf)
-    rel_f, _ = check_y(yf.cpu().numpy()[rows], Ys)
-    print(f"[full] {name}: fused form sampled rel L2 {rel_f:.2e}")
+    rel_f, _ = check_y(yf.cpu().numpy(), Y)
+    print(f"[full] {name}: fused form whole-tensor rel L2 {rel_f:.2e}")
 
 
 @pytest.mark.parametrize("name", ["ffn1p5b", "ffn1p5b_heavytail"])
