@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     dense_ffn_forward,
     ffn_backward,
     ffn_forward,
+    ffn_forward_static,
     fused_updown,
     gate_pack,
     gather_rows,

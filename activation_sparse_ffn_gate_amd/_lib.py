@@ -57,6 +57,7 @@ _SIGNATURES = {
     "twell_sliced_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
+    "twell_ffn_forward_static": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "twell_column_activity": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_live_layout": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, ctypes.POINTER(_I64)]),
@@ -296,6 +297,18 @@ def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None, ctrl=Non
     cb = _workspace(ctrl, x.device, zeroed=True)
     cp, cn = cb.get(ctrl_bytes(M))
     _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, _stream(x)), "twell_ffn_forward")
+    return y
+
+
+def ffn_forward_static(x, Wg, WuT, Wd, T: int, C: int, y=None):
+    """twell_ffn_forward_static: the forward for up to 256 rows with the
+    library's static scratch buffer (nothing allocated by the library; y is
+    allocated here only when not given)."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    _check(lib().twell_ffn_forward_static(*args, M, d, F, T, C, _dptr(y), _stream(x)), "twell_ffn_forward_static")
     return y
 
 

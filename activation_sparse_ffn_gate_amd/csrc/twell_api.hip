@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/twell.h"
 #include "twell_internal.hpp"
@@ -239,6 +240,87 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   return hip_status(twell::launch_dense(a, s));
 }
 
+// The forward up to twell::kFewRows rows: the small-batch gate spills the z
+// of every overflowing (row, tile) into `spill`, and the fused kernel (a
+// workgroup per row) does overflow rows from it: two launches in all. Long
+// rows are cut over several workgroups, with their partial rows in `part`
+// (splits * M * d floats) and one arrival counter per row after the control
+// block's flags.
+int splits_for(int64_t M) { return int(std::min<int64_t>(16, std::max<int64_t>(1, 512 / M))); }
+
+int few_rows_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd, int64_t M,
+                     int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl, const twell_packed& p,
+                     float* spill, float* part, hipStream_t s) {
+  int st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill);
+  if (st != TWELL_OK) return st;
+  twell::FusedArgs a = fused_args(x, WuT, Wd, &p, M, d, F, T, C, y);
+  a.spill = spill;
+  a.splits = splits_for(M);
+  a.part = part;
+  a.counters = fallback_counters(ctrl, M);
+  return hip_status(twell::launch_fused_updown(a, s));
+}
+
+// ------------------------------------------------ allocation-free forward
+// One static device buffer per GPU for twell_ffn_forward_static: the control
+// block (sized for the most rows that entry takes), then the packing, the
+// spill and the partial rows of the call. It starts zeroed when the code
+// object is loaded; the control block in it is left zeroed by every call, as
+// for a caller-owned one. Host code never names the array in an argument:
+// it uses the address hipGetSymbolAddress returned on that device.
+constexpr size_t kStaticScratch = TWELL_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratch];
+
+struct StaticLayout {
+  size_t ctrl = 0, vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, spill = 0, part = 0, total = 0;
+};
+
+StaticLayout static_layout(int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
+  StaticLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t m = size_t(M), nT = size_t(F / T);
+  L.ctrl = take(ctrl_bytes(twell::kFewRows));
+  L.vals = take(m * nT * size_t(C) * 4);
+  L.idx = take(m * nT * size_t(C));
+  L.counts = take(m * nT * 2);
+  L.ovf_rows = take(m * 4);
+  L.n_ovf = take(4);
+  L.spill = take(m * size_t(F) * 4);
+  L.part = take(size_t(splits_for(std::max<int64_t>(M, 1))) * m * size_t(d) * 4);
+  L.total = off;
+  return L;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the stream's device, taken once per device
+// with that device current.
+int static_scratch(hipStream_t s, uint8_t** out) {
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return TWELL_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TWELL_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return TWELL_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return TWELL_E_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr) return TWELL_E_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<uint8_t*>(g_scratch[dev]);
+  return TWELL_OK;
+}
+
 // Workspace of twell_ffn_backward: row offsets, the counting sort's per-block
 // counts and unit offsets, and the entry list (unit, row, h, dz, du) with its
 // unit-major order.
@@ -440,20 +522,11 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
   if (M <= twell::kFewRows) {
-    // Few rows (the small-batch gate's range): it spills the z of every overflowing
-    // (row, tile) into the fallback's region, and the fused kernel (a
-    // workgroup per row) does overflow rows from it: two launches in all.
-    // Long rows are cut over several workgroups (partial rows in the split-K
-    // region, one arrival counter per row among the fallback's, both idle here).
-    float* spill = at<float>(workspace, L.h_hi);  // M F floats: the region holds 2 M F bf16
-    st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill);
-    if (st != TWELL_OK) return st;
-    twell::FusedArgs a = fused_args(x, WuT, Wd, &p, M, d, F, T, C, y);
-    a.spill = spill;
-    a.splits = int(std::min<int64_t>(16, std::max<int64_t>(1, 512 / M)));  // splits M <= 512 rows of d floats
-    a.part = at<float>(workspace, L.split);
-    a.counters = fallback_counters(ctrl, M);
-    return hip_status(twell::launch_fused_updown(a, s));
+    // The spill (M F floats) takes the fallback's hidden pair (2 M F bf16) and
+    // the partial rows (at most 512 rows of d floats) its split-K region; both
+    // are idle on this path.
+    return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, p, at<float>(workspace, L.h_hi),
+                            at<float>(workspace, L.split), s);
   }
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
@@ -465,6 +538,31 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   return dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                     at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
                     fallback_counters(ctrl, M), s);
+}
+
+int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                             int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* stream) {
+  if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
+  if (st == TWELL_OK && M > twell::kFewRows) st = TWELL_E_UNSUPPORTED;
+  if (st != TWELL_OK) return st;
+  const StaticLayout L = static_layout(M, d, F, T, C);
+  if (L.total > kStaticScratch) return TWELL_E_SCRATCH;
+  if (M == 0) return TWELL_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* base = nullptr;
+  st = static_scratch(s, &base);
+  if (st != TWELL_OK) return st;
+  twell_packed p;
+  p.vals = reinterpret_cast<float*>(base + L.vals);
+  p.idx = base + L.idx;
+  p.counts = reinterpret_cast<uint16_t*>(base + L.counts);
+  p.ovf_rows = reinterpret_cast<int32_t*>(base + L.ovf_rows);
+  p.n_ovf = reinterpret_cast<int32_t*>(base + L.n_ovf);
+  return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, base + L.ctrl, p,
+                          reinterpret_cast<float*>(base + L.spill), reinterpret_cast<float*>(base + L.part), s);
 }
 
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
@@ -563,6 +661,7 @@ const char* twell_status_string(int32_t status) {
     case TWELL_E_UNSUPPORTED: return "unsupported shape (T, C, F % T or d)";
     case TWELL_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case TWELL_E_HIP: return "HIP launch failed";
+    case TWELL_E_SCRATCH: return "shape needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 4
+#define TWELL_ABI_VERSION 5
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -62,6 +62,7 @@ extern "C" {
 #define TWELL_E_UNSUPPORTED (-2) /* F % T != 0, T not in {64,128}, C out of [1,T], d not supported */
 #define TWELL_E_WORKSPACE (-3)   /* workspace or control block null, misaligned or too small */
 #define TWELL_E_HIP (-4)         /* a HIP launch failed (hipGetLastError) */
+#define TWELL_E_SCRATCH (-5)     /* twell_ffn_forward_static: shape past its static buffer */
 
 /* Operations for twell_workspace_bytes. */
 #define TWELL_OP_GATE_PACK 0
@@ -164,6 +165,26 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
                       const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
                       float* y, void* ctrl, size_t ctrl_bytes, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/* Allocation-free form of twell_ffn_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * hipMalloc): no workspace or control block is passed. Up to 256 rows (the
+ * decode and batched-decode range), the same kernels and the same result, bit
+ * for bit, as twell_ffn_forward; y [M, d] fp32 is fully written.
+ * Scratch: one static device buffer of TWELL_STATIC_SCRATCH_BYTES per GPU,
+ * held from the library's first use on that GPU until the process ends. It
+ * holds a control block sized for 256 rows, the packing (M (F/T) C 5 +
+ * M (F/T) 2 + 4 M bytes), the z of overflowing tiles (M F 4 bytes) and the
+ * partial rows of long rows (min(16, 512 / M) M d 4 bytes), each rounded up
+ * to 256 bytes. Every call on one GPU uses the same buffer: calls that may
+ * overlap on a GPU (several streams or threads) race, and the caller must
+ * order them. Returns TWELL_E_UNSUPPORTED for M > 256, TWELL_E_SCRATCH when
+ * the shape needs more than the buffer, TWELL_E_HIP when the buffer's device
+ * address cannot be taken; argument rules otherwise as twell_ffn_forward. */
+#define TWELL_STATIC_SCRATCH_BYTES (32u << 20)
+int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T,
+                             int32_t C, float* y, void* stream);
 
 /* Dense MFMA gated-FFN baseline (the comparator the pages measure against:
  * dense matmuls, tgviewer.app Telegram post, paragraph after "Обучение"):

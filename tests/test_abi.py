@@ -23,8 +23,8 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 4
-    for s in (OK, E_ARG, E_UNSUP, E_WS, -4):
+    assert L.twell_abi_version() == 5
+    for s in (OK, E_ARG, E_UNSUP, E_WS, -4, -5):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"
 
@@ -273,3 +273,20 @@ def test_row_and_unit_limits():
     assert L.twell_gate_pack(FAKE, FAKE, M_max, 256, 1024, 64, 8, ctypes.byref(pk), None, FAKE,
                              tw.ctrl_bytes(M_max), None) == E_UNSUP
     assert L.twell_gate_pack(FAKE, FAKE, 64, 256, F_max, 128, 8, ctypes.byref(pk), None, FAKE, g, None) == E_UNSUP
+
+
+def test_static_forward_validation():
+    """twell_ffn_forward_static refuses, before any HIP call, more than 256
+    rows, shapes whose scratch passes its static buffer, and bad arguments;
+    M = 0 is a no-op."""
+    L = tw.lib()
+    f = L.twell_ffn_forward_static
+    E_SCRATCH = -5
+    assert "static buffer" in tw.status_string(E_SCRATCH)
+    assert f(FAKE, FAKE, FAKE, FAKE, 257, 2048, 8192, 128, 16, FAKE, None) == E_UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 2048, 8192, 96, 16, FAKE, None) == E_UNSUP
+    assert f(FAKE, FAKE, None, FAKE, 256, 2048, 8192, 128, 16, FAKE, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 2048, 8192, 128, 16, None, None) == E_ARG
+    # 256 rows of F = 32768: the z spill alone is 32 MiB
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 1024, 32768, 128, 16, FAKE, None) == E_SCRATCH
+    assert f(None, FAKE, FAKE, FAKE, 0, 2048, 8192, 128, 16, None, None) == OK
