@@ -49,24 +49,20 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
       L.ovf_rows = take(m * 4);
       L.n_ovf = take(4);
       break;
-    case TWELL_OP_FFN_FORWARD: {
+    case TWELL_OP_FFN_FORWARD:
       L.vals = take(m * nT * size_t(C) * 4);
       L.idx = take(m * nT * size_t(C));
       L.counts = take(m * nT * 2);
       L.ovf_rows = take(m * 4);
       L.n_ovf = take(4);
-      // The up/down kernels' buffers and the fallback's (hidden pair and
-      // partial tiles) are live at different times of the stream, so they
-      // share one region.
-      const size_t h_bytes = align256(m * f * 2);
-      const size_t fb_bytes = 2 * h_bytes + twell::kDenseSplitBytes;
-      const size_t scratch = take(std::max(fb_bytes, twell::sliced_layout(M, F, T, C).total));
-      L.part = scratch;
-      L.h_hi = scratch;
-      L.h_lo = scratch + h_bytes;
-      L.split = scratch + 2 * h_bytes;
+      // The up/down kernels and the fallback run concurrently (two streams),
+      // so each has its own region: the sliced kernels' partials, then the
+      // fallback's hidden pair and partial tiles.
+      L.part = take(twell::sliced_layout(M, F, T, C).total);
+      L.h_hi = take(m * f * 2);
+      L.h_lo = take(m * f * 2);
+      L.split = take(twell::kDenseSplitBytes);
       break;
-    }
     case TWELL_OP_SLICED_UPDOWN:
       L.part = take(twell::sliced_layout(M, F, T, C).total);
       break;
@@ -300,12 +296,13 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch[kMaxDevices] = {};
 
+int stream_device(hipStream_t s, int* dev);
+
 // Device address of `scratch` on the stream's device, taken once per device
 // with that device current.
 int static_scratch(hipStream_t s, uint8_t** out) {
   int dev = -1;
-  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return TWELL_E_HIP;
-  if (dev < 0 || dev >= kMaxDevices) return TWELL_E_HIP;
+  if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch[dev] == nullptr) {
     int cur = -1;
@@ -318,6 +315,55 @@ int static_scratch(hipStream_t s, uint8_t** out) {
     g_scratch[dev] = ptr;
   }
   *out = static_cast<uint8_t*>(g_scratch[dev]);
+  return TWELL_OK;
+}
+
+// ------------------------------------------------ fallback side stream
+// Above the few-row range the dense fallback of overflow rows does not depend
+// on the up/down kernels (they write disjoint rows of y and use disjoint
+// workspace regions), so it runs on a second stream of the caller's device,
+// forked after the gate and joined before the call returns (stream order of
+// the caller's stream is kept). With no overflow row its two launches end at
+// once and hide behind the up/down kernels; with overflow rows the two paths
+// overlap. One non-blocking stream at the default priority and two events per
+// device, created on the first forward on that device and kept for the
+// process; the fork and join of one call are issued under a lock, so calls
+// from several host threads pair their events correctly (their fallbacks then
+// run one after the other on the side stream).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+int stream_device(hipStream_t s, int* dev) {
+  if ((s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev)) != hipSuccess) return TWELL_E_HIP;
+  return (*dev >= 0 && *dev < kMaxDevices) ? TWELL_OK : TWELL_E_HIP;
+}
+
+// Creates the side stream and events of device `dev` if needed; call with
+// g_side_mu held.
+int side_stream_locked(int dev, SideStream** out) {
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return TWELL_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return TWELL_E_HIP;
+    SideStream n;
+    bool ok = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (!ok) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s) (void)hipStreamDestroy(n.s);
+      return TWELL_E_HIP;
+    }
+    ss = n;
+  }
+  *out = &ss;
   return TWELL_OK;
 }
 
@@ -528,16 +574,29 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, p, at<float>(workspace, L.h_hi),
                             at<float>(workspace, L.split), s);
   }
+  int dev = -1;
+  if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* ss = nullptr;
+  st = side_stream_locked(dev, &ss);  // before anything is enqueued
+  if (st != TWELL_OK) return st;
   st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
   if (st != TWELL_OK) return st;
+  // fork: the fallback of the overflow rows on the side stream
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return TWELL_E_HIP;
+  const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
+                               at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
+                               fallback_counters(ctrl, M), ss->s);
+  // join before anything else can be reported, so the caller's stream never
+  // runs ahead of work already on the side stream
+  const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
   if (twell::sliced_supports(d, F))
     st = sliced_impl(x, WuT, Wd, &p, M, d, F, T, C, at<uint8_t>(workspace, L.part), y, s);
   else
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
-  if (st != TWELL_OK) return st;
-  return dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
-                    at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                    fallback_counters(ctrl, M), s);
+  if (!joined || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return TWELL_E_HIP;
+  return st != TWELL_OK ? st : st_fb;
 }
 
 int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,

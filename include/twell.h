@@ -14,7 +14,9 @@
  *  - bf16 tensors are passed as raw uint16_t bit patterns.
  *  - Every array argument is a DEVICE pointer to row-major, contiguous memory
  *    allocated and owned by the caller. The library never allocates or frees
- *    memory and keeps no state between calls.
+ *    device memory. What it keeps per GPU for the process: the static buffer
+ *    of twell_ffn_forward_static, and a side stream with two events that
+ *    twell_ffn_forward creates on its first call on that GPU (above 256 rows).
  *  - Weights are all [F, d] row-major, row j belonging to hidden unit j:
  *      Wg  = gate_proj.weight, WuT = up_proj.weight,
  *      Wd  = down_proj.weight transposed (row j = the d outputs unit j feeds).
@@ -153,10 +155,16 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
  * paragraph 3; the gate epilogue feeding a fused up/down pipeline: Tencent
  * Cloud article, section 2), plus the dense path for rows that overflow the
  * packing (Telegram post, part "Обучение"; Tencent Cloud article, section 3).
- * One stream, no host synchronisation, the packing kept in the workspace (see
+ * No host synchronisation, the packing kept in the workspace (see
  * twell_packed_view); y [M, d] fp32 is fully written.
  * Above 256 rows: twell_gate_pack, then twell_sliced_updown (twell_fused_updown
- * for the d that the sliced form does not support), then twell_dense_fallback.
+ * for the d that the sliced form does not support) on `stream` and, at the
+ * same time, twell_dense_fallback on a side stream of the same GPU (forked
+ * after the gate, joined into `stream` before the call returns, so work the
+ * caller enqueues on `stream` afterwards sees the whole y). The side stream
+ * and its two events are created on the first such call on a GPU (call it
+ * once outside HIP graph capture first) and serialise the fallbacks of
+ * concurrent callers on that GPU.
  * Up to 256 rows: the gate also keeps every z of each (row, tile) whose count
  * exceeds C in the workspace, and the fused kernel does overflow rows from it
  * (their whole active set, still only gathers): two launches, no fallback.
