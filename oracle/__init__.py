@@ -23,11 +23,14 @@ from .twell_oracle import (  # noqa: F401
     ffn_from_active_set,
     ffn_backward,
     ffn_backward_from_hybrid,
+    ffn_from_hidden_packing,
     ffn_from_twell,
     gate_preactivations,
     hybrid_pack,
     live_layout,
     overflow_rows,
     pack_twell,
+    pack_twell_hidden,
     unpack_twell,
+    up_projections,
 )

@@ -208,6 +208,57 @@ def ffn_from_active_set(x, WuT, Wd, Z: np.ndarray) -> np.ndarray:
     return _sum_over_terms(x, WuT, Wd, r, j, Z[r, j], Z.shape[0])
 
 
+# --------------------------------------------------------- gate-only variant
+# A variant of the inference path that is not on the pages: the gate and up
+# products are formed densely together, the packing stores the hidden value
+# h = ReLU(z) * u instead of g, and the down product gathers only the Wd rows
+# of stored units. The active set stays the gate's ([tencent] section 1: the
+# gate decides which units are live), so a unit with z > 0 is stored even when
+# its h is zero or negative. Rows that overflow a tile take the dense path, as
+# in the main forward ([tgviewer] "Обучение"; [tencent] section 3).
+def up_projections(x: np.ndarray, WuT: np.ndarray, rows=None) -> np.ndarray:
+    """U = x WuT^T in fp64, shape [M, F] (the up projection of every unit)."""
+    X = decode_bf16(x if rows is None else x[rows])
+    return X @ decode_bf16(WuT).T
+
+
+def pack_twell_hidden(Z: np.ndarray, H: np.ndarray, T: int, C: int) -> TwellPacking:
+    """TwELL packing of the hidden values H at the units the gate activates.
+
+    Counts, slots, tile-local indices and the overflow set are those of
+    pack_twell(Z, T, C) (active iff Z > 0, ascending column order, counts not
+    clamped); the value kept in a slot is H at that unit instead of ReLU(Z).
+    """
+    Z, H = np.asarray(Z), np.asarray(H)
+    if Z.shape != H.shape:
+        raise ValueError("Z and H must have the same shape")
+    p = pack_twell(Z, T, C)
+    M = Z.shape[0]
+    used = np.arange(C)[None, None, :] < np.minimum(p.counts.astype(np.int64), C)[:, :, None]
+    r, t, s = np.nonzero(used)
+    vals = np.zeros((M, p.n_tiles, C), dtype=H.dtype)
+    vals[r, t, s] = H.reshape(M, p.n_tiles, T)[r, t, p.idx[r, t, s].astype(np.int64)]
+    return TwellPacking(p.counts, p.idx, vals, p.ovf, T, C)
+
+
+def ffn_from_hidden_packing(p: TwellPacking, x, Wg, WuT, Wd) -> np.ndarray:
+    """y from a packing of hidden values, fp64: for a row that fits,
+    y_r = sum over its stored units j of h_j * Wd[j]; overflow rows take the
+    dense definition."""
+    M = p.counts.shape[0]
+    D = decode_bf16(Wd)
+    fits = np.ones(M, dtype=bool)
+    fits[p.ovf] = False
+    used = np.minimum(p.counts.astype(np.int64), p.C)
+    r, t, s = np.nonzero((np.arange(p.C)[None, None, :] < used[:, :, None]) & fits[:, None, None])
+    j = t * p.T + p.idx[r, t, s].astype(np.int64)
+    Hs = sps.csr_matrix((p.vals[r, t, s].astype(np.float64), (r, j)), shape=(M, D.shape[0]))
+    y = np.asarray(Hs @ D)
+    if len(p.ovf):
+        y[p.ovf] = dense_gated_ffn(x, Wg, WuT, Wd, rows=p.ovf)
+    return y
+
+
 def column_rms(Z: np.ndarray) -> np.ndarray:
     """Root-mean-square of each column of Z over all rows (tokens)."""
     Z = np.asarray(Z, dtype=np.float64)

@@ -31,6 +31,14 @@ What pins what:
                          reserve rows kept whole as dense g rows).
 * ffn_backward_from_hybrid  equal to the dense definition, reserve rows
                          included.
+* up_projections /
+  pack_twell_hidden /
+  ffn_from_hidden_packing   (gate-only variant) a hand-worked example with a
+                         negative and a zero h at active units and an overflow
+                         row (tests/golden/); exact integer brute force; with
+                         H = ReLU(Z) the hidden packing is the gate packing bit
+                         for bit; the sum over stored h_j Wd[j] equals the
+                         dense definition, overflow rows included.
 * column_activity,
   live_layout,
   compact_rows           hand-worked cases (strict activity, ascending order,
@@ -87,6 +95,7 @@ def golden(name):
 
 HAND = golden("forward_hand_example.json")
 HAND_BWD = golden("backward_hand_example.json")
+HAND_GU = golden("gateup_hand_example.json")
 
 
 # --------------------------------------------------------------------- pins
@@ -412,6 +421,68 @@ def pin_backward_hybrid_equals_dense(o):
         assert np.abs(a - b).max() <= 1e-6 * max(np.abs(b).max(), 1e-300)
 
 
+def pin_gateup_hand_example(o):
+    """The gate-only variant's hand-worked example: h < 0 and h = 0 at active
+    units are stored, the overflow row takes the dense path."""
+    h = {k: bf(v) for k, v in HAND_GU.items() if k in ("x", "Wg", "WuT", "Wd")}
+    Z = o.gate_preactivations(h["x"], h["Wg"])
+    U = o.up_projections(h["x"], h["WuT"])
+    assert np.array_equal(Z, np.array(HAND_GU["z"], dtype=np.float64))
+    assert np.array_equal(U, np.array(HAND_GU["u"], dtype=np.float64))
+    H = np.array(HAND_GU["h"], dtype=np.float32)
+    p = o.pack_twell_hidden(Z.astype(np.float32), H, HAND_GU["T"], HAND_GU["C"])
+    assert p.counts.tolist() == HAND_GU["counts"]
+    for r in range(2):
+        for t in range(2):
+            if HAND_GU["idx0"][r][t] is not None:
+                assert int(p.idx[r, t, 0]) == HAND_GU["idx0"][r][t]
+                assert float(p.vals[r, t, 0]) == HAND_GU["val0"][r][t]
+    assert sorted(int(r) for r in p.ovf) == HAND_GU["overflow_rows"]
+    y = o.ffn_from_hidden_packing(p, h["x"], h["Wg"], h["WuT"], h["Wd"])
+    assert np.array_equal(y, np.array(HAND_GU["y"], dtype=np.float64))
+
+
+def pin_up_integer_bruteforce(o):
+    """x WuT^T on small integers, against Python-int triple loops."""
+    rng = np.random.default_rng(21)
+    M, d, F = 3, 5, 4
+    xi = rng.integers(-8, 9, size=(M, d))
+    wi = rng.integers(-8, 9, size=(F, d))
+    want = [[sum(int(xi[r, k]) * int(wi[j, k]) for k in range(d)) for j in range(F)] for r in range(M)]
+    got = o.up_projections(bf(xi), bf(wi))
+    assert got.tolist() == want
+    assert o.up_projections(bf(xi), bf(wi), rows=np.array([2, 0])).tolist() == [want[2], want[0]]
+
+
+def pin_hidden_pack_reduces_to_gate_pack(o):
+    """With H = ReLU(Z) the hidden packing is the gate packing, bit for bit."""
+    rng = np.random.default_rng(22)
+    Z = rng.standard_normal((11, 48)).astype(np.float32)
+    Z[rng.random(Z.shape) < 0.2] = 0.0
+    for T, C in ((8, 2), (16, 16), (48, 3)):
+        a = o.pack_twell_hidden(Z, np.maximum(Z, 0), T, C)
+        b = o.pack_twell(Z, T, C)
+        assert np.array_equal(a.counts, b.counts) and np.array_equal(a.ovf, b.ovf)
+        used = np.arange(C)[None, None, :] < np.minimum(b.counts, C)[:, :, None]
+        assert np.array_equal(a.idx[used], b.idx[used])
+        assert np.array_equal(a.vals[used].view(np.uint32), b.vals[used].view(np.uint32))
+
+
+def pin_hidden_ffn_equals_dense(o):
+    """Sum over stored h_j Wd[j] (dense for overflow rows) is the definition."""
+    rng = np.random.default_rng(23)
+    M, d, F, T, C = 9, 16, 24, 8, 4
+    x = rand_bf16(rng, (M, d))
+    Wg, WuT, Wd = (rand_bf16(rng, (F, d), 0.5) for _ in range(3))
+    Z = o.gate_preactivations(x, Wg)
+    H = np.maximum(Z, 0) * o.up_projections(x, WuT)
+    p = o.pack_twell_hidden(Z, H, T, C)
+    assert 0 < len(p.ovf) < M  # both kinds of rows occur
+    y = o.ffn_from_hidden_packing(p, x, Wg, WuT, Wd)
+    want = o.dense_gated_ffn(x, Wg, WuT, Wd)
+    assert np.abs(y - want).max() <= 1e-12 * np.abs(want).max()
+
+
 PINS = [
     pin_decode, pin_hand_example, pin_integer_bruteforce, pin_relu_identity, pin_all_active,
     pin_zero_density, pin_pack_csr, pin_pack_rowwise_ell, pin_pack_strict, pin_overflow_boundary,
@@ -419,6 +490,8 @@ PINS = [
     pin_column_activity, pin_live_layout, pin_compact_rows, pin_compaction_keeps_ffn,
     pin_backward_hand_example, pin_backward_finite_difference, pin_hybrid_pack,
     pin_backward_hybrid_equals_dense,
+    pin_gateup_hand_example, pin_up_integer_bruteforce, pin_hidden_pack_reduces_to_gate_pack,
+    pin_hidden_ffn_equals_dense,
 ]
 
 
@@ -560,6 +633,14 @@ MUTANTS = {
     "hybrid_ge_k": dict(hybrid_pack=lambda Z, K: _hybrid_variant("ge", Z, K)),
     "hybrid_descending": dict(hybrid_pack=lambda Z, K: _hybrid_variant("desc", Z, K)),
     "hybrid_reserve_z": dict(hybrid_pack=lambda Z, K: _hybrid_variant("res_z", Z, K)),
+    "hidden_activity_from_h": dict(pack_twell_hidden=lambda Z, H, T, C: O.pack_twell_hidden(H, H, T, C)),
+    "hidden_stores_g": dict(pack_twell_hidden=lambda Z, H, T, C: O.pack_twell_hidden(Z, np.maximum(Z, 0), T, C)),
+    "hidden_down_ignores_overflow": dict(ffn_from_hidden_packing=lambda p, *a: O.ffn_from_hidden_packing(
+        O.TwellPacking(p.counts, p.idx, p.vals, np.zeros(0, dtype=np.int64), p.T, p.C), *a)),
+    "hidden_down_uses_up": dict(ffn_from_hidden_packing=lambda p, x, Wg, WuT, Wd: O.ffn_from_hidden_packing(
+        p, x, Wg, WuT, WuT)),
+    "up_not_transposed": dict(up_projections=lambda x, WuT, rows=None: O.decode_bf16(
+        x if rows is None else x[rows]) @ O.decode_bf16(WuT)),
     "hybrid_bwd_drops_reserve": dict(ffn_backward_from_hybrid=lambda h, *a: O.ffn_backward_from_hybrid(
         O.HybridFormat(h.idx, h.vals, h.count, h.res_rows[:0], h.res_vals[:0]), *a)),
 }
