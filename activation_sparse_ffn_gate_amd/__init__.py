@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     OP_DENSE_FALLBACK,
     OP_DENSE_FFN,
     OP_FFN_FORWARD,
+    OP_FFN_FORWARD_GATEUP,
     OP_GATE_PACK,
     OP_SLICED_UPDOWN,
     LIB_PATH,
@@ -26,10 +27,13 @@ from ._lib import (  # noqa: F401
     ffn_backward,
     ffn_forward,
     ffn_forward_static,
+    ffn_forward_gateup,
     fused_updown,
     gate_pack,
+    gateup_pack,
     gather_rows,
     header_functions,
+    hidden_down,
     hybrid_pack,
     lib,
     live_layout,

@@ -19,6 +19,7 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "twell.h")
 
 TWELL_OK = 0
 OP_GATE_PACK, OP_FFN_FORWARD, OP_DENSE_FFN, OP_DENSE_FALLBACK, OP_SLICED_UPDOWN, OP_COLUMN_ACTIVITY = 0, 1, 2, 3, 4, 5
+OP_FFN_FORWARD_GATEUP = 6
 
 
 class TwellError(RuntimeError):
@@ -58,6 +59,10 @@ _SIGNATURES = {
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward_static": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
+    "twell_gateup_pack": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _P, _SZ, _P]),
+    "twell_hidden_down": (ctypes.c_int, [_P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
+    "twell_ffn_forward_gateup": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ,
+                                                _P]),
     "twell_dense_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "twell_column_activity": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_live_layout": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, ctypes.POINTER(_I64)]),
@@ -297,6 +302,55 @@ def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None, ctrl=Non
     cb = _workspace(ctrl, x.device, zeroed=True)
     cp, cn = cb.get(ctrl_bytes(M))
     _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, _stream(x)), "twell_ffn_forward")
+    return y
+
+
+def gateup_pack(x, Wg, WuT, T: int, C: int, out: Packed | None = None, z_debug=None, h_debug=None,
+                ctrl=None) -> Packed:
+    """twell_gateup_pack: dense gate and up products, h packed in TwELL.
+    z_debug / h_debug: both None or both float32 [M, F] tensors."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    px, pg, pu = _bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d))
+    out = out or Packed.empty(M, F, T, C, x.device)
+    pz = ph = ctypes.c_void_p(0)
+    if z_debug is not None or h_debug is not None:
+        _f32_out(z_debug, "z_debug", (M, F), x.device)
+        _f32_out(h_debug, "h_debug", (M, F), x.device)
+        pz, ph = _dptr(z_debug), _dptr(h_debug)
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    pk = out._c()
+    _check(lib().twell_gateup_pack(px, pg, pu, M, d, F, T, C, ctypes.byref(pk), pz, ph, cp, cn, _stream(x)),
+           "twell_gateup_pack")
+    return out
+
+
+def hidden_down(Wd, packed: Packed, y):
+    """twell_hidden_down: y rows of non-overflow rows from a packing of h."""
+    M, d = y.shape
+    F = Wd.shape[0]
+    pw = _bf16(Wd, "Wd", (F, d))
+    y = _f32_out(y, "y", (M, d), Wd.device)
+    pk = packed._c()
+    _check(lib().twell_hidden_down(pw, ctypes.byref(pk), M, d, F, packed.T, packed.C, _dptr(y), _stream(Wd)),
+           "twell_hidden_down")
+    return y
+
+
+def ffn_forward_gateup(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None, ctrl=None):
+    """twell_ffn_forward_gateup: the gate-only variant of the forward."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    need = max(workspace_bytes(OP_FFN_FORWARD_GATEUP, M, d, F, T, C), workspace_bytes(OP_FFN_FORWARD, M, d, F, T, C))
+    wp, wn = ws.get(need)  # also large enough for packed_view
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    _check(lib().twell_ffn_forward_gateup(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, _stream(x)),
+           "twell_ffn_forward_gateup")
     return y
 
 

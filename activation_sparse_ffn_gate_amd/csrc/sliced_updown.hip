@@ -326,6 +326,105 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs
   }
 }
 
+// Down product of the gate-only variant: the packing holds h itself, so one
+// pass does it. Wave per (row, slice s): the row's stored units and their h
+// are staged from the packing (as the up pass stages units and g), then
+// y_r[s] = sum_e h_e * Wd[j_e][s] exactly as in the down pass. Overflow rows
+// are left untouched (the dense fallback owns them).
+template <int L, int V, int U>
+__global__ __launch_bounds__(64 * kRowsPerWG) void hidden_down_kernel(SlicedArgs a) {
+  constexpr int G = 64 / L;
+  __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
+  __shared__ float s_h[kRowsPerWG][kListCap + kListPad];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slice = blockIdx.x % kSlices;
+  const int row = (blockIdx.x / kSlices) * kRowsPerWG + w;
+  if (row >= a.M) return;
+
+  const int nT = a.F / a.T;
+  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
+  int c[kCountGroups];
+  bool over = false;
+#pragma unroll
+  for (int q = 0; q < kCountGroups; ++q) {
+    const int t = q * 64 + lane;
+    c[q] = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
+    over |= c[q] > a.C;
+  }
+  for (int t = 64 * kCountGroups + lane; t < nT; t += 64) over |= cnt_row[t] > a.C;
+  if (__ballot(over) != 0) return;  // owned by the dense fallback
+
+  const int grp = (G == 1) ? 0 : lane / L;
+  const int li = (G == 1) ? min(lane, L - 1) : lane % L;  // idle lanes repeat the last piece
+  const int col0 = slice * (a.d / kSlices) + li * 8;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const uint32_t col_bytes = static_cast<uint32_t>(col0) * 2u;
+  int* lj = s_j[w];
+  float* lh = s_h[w];
+
+  float acc[V][8];
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[v][k] = 0.f;
+
+  stage_row<true>(a, row, c, lj, lh, [&](int n, int) {
+    static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the list");
+    if (lane < kListPad) {  // pad to a whole step: unit 0 (a valid row), h 0
+      lj[n + lane] = 0;
+      lh[n + lane] = 0.f;
+    }
+    wave_lds_sync();
+    for (int e = 0; e < n; e += G * U) {
+      u32x4_t wd[U][V];
+      float hv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = e + u * G + grp;
+        hv[u] = lh[k];
+        const uint32_t off = static_cast<uint32_t>(lj[k]) * row_bytes + col_bytes;
+#pragma unroll
+        for (int v = 0; v < V; ++v) wd[u][v] = ldg16(a.Wd, off + v * 16 * L);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[v][2 * q] = fmaf(hv[u], bf16_lo(wd[u][v][q]), acc[v][2 * q]);
+            acc[v][2 * q + 1] = fmaf(hv[u], bf16_hi(wd[u][v][q]), acc[v][2 * q + 1]);
+          }
+    }
+  });
+
+  static_for<0, 6>([&](auto I) {
+    constexpr int X = 1 << I.value;
+    if constexpr (X >= L && X < 64) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if constexpr (X == 32)
+            acc[v][k] = sum_halves(acc[v][k]);
+          else
+            acc[v][k] += xor_lanes<X>(acc[v][k]);
+        }
+    }
+  });
+
+  float* yr = a.y + static_cast<size_t>(row) * a.d + col0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if (v % G == grp && (G > 1 || lane < L)) {
+      *reinterpret_cast<float4*>(yr + v * 8 * L) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+      *reinterpret_cast<float4*>(yr + v * 8 * L + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+    }
+  }
+}
+
 // Loads in flight per lane per step. Up pass: about 8 sixteen-byte vectors.
 // Down pass: about 4 (deeper unrolling costs more in occupancy than it gains).
 template <int L, int V>
@@ -346,6 +445,12 @@ hipError_t launch_up(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) 
 template <int L, int V>
 hipError_t launch_down(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
   sliced_down_kernel<L, V, unroll_down<V>()><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int L, int V>
+hipError_t launch_hdown(const SlicedArgs& a, hipStream_t s, dim3 grid, dim3 block) {
+  hidden_down_kernel<L, V, unroll_down<V>()><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -431,6 +536,20 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s) {
     default: break;
   }
   return e;
+}
+
+hipError_t launch_hidden_down(const SlicedArgs& a, hipStream_t s) {
+  int L, V;
+  if (!sliced_supports(a.d, a.F)) return hipErrorInvalidValue;
+  lane_split_down(a.d, &L, &V);
+  const dim3 grid(((a.M + kRowsPerWG - 1) / kRowsPerWG) * kSlices), block(64 * kRowsPerWG);
+  switch (L * 16 + V) {
+#define TWELL_CASE(L, V) \
+  case L * 16 + V: return launch_hdown<L, V>(a, s, grid, block);
+    TWELL_DOWN_SHAPES(TWELL_CASE)
+#undef TWELL_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace twell

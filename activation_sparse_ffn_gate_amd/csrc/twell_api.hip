@@ -66,6 +66,16 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
     case TWELL_OP_SLICED_UPDOWN:
       L.part = take(twell::sliced_layout(M, F, T, C).total);
       break;
+    case TWELL_OP_FFN_FORWARD_GATEUP:  // packing of h, then the fallback's region
+      L.vals = take(m * nT * size_t(C) * 4);
+      L.idx = take(m * nT * size_t(C));
+      L.counts = take(m * nT * 2);
+      L.ovf_rows = take(m * 4);
+      L.n_ovf = take(4);
+      L.h_hi = take(m * f * 2);
+      L.h_lo = take(m * f * 2);
+      L.split = take(twell::kDenseSplitBytes);
+      break;
     case TWELL_OP_DENSE_FFN:
       L.h_hi = take(m * f * 2);
       break;
@@ -234,6 +244,50 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   a.counters = counters;
   a.counter_base = 0;
   return hip_status(twell::launch_dense(a, s));
+}
+
+// Gate-only variant: dense gate and up products with h packed in TwELL.
+int gateup_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, int64_t M, int64_t d, int64_t F,
+                int32_t T, int32_t C, const twell_packed* out, float* z_debug, float* h_debug, uint32_t* ctrl,
+                hipStream_t s) {
+  if (M == 0) return hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
+  twell::GateArgs a;
+  a.x = x;
+  a.Wg = Wg;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.vals = out->vals;
+  a.idx = out->idx;
+  a.counts = out->counts;
+  a.ovf_rows = out->ovf_rows;
+  a.n_ovf = out->n_ovf;
+  a.ctrl = ctrl;
+  a.z_debug = z_debug;
+  a.col_active = nullptr;
+  a.spill = nullptr;
+  a.WuT = WuT;
+  a.h_debug = h_debug;
+  return hip_status(twell::launch_gateup_pack(a, s));
+}
+
+int hidden_down_impl(const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                     int32_t C, float* y, hipStream_t s) {
+  if (M == 0) return TWELL_OK;
+  twell::SlicedArgs a{};
+  a.Wd = Wd;
+  a.vals = in->vals;
+  a.idx = in->idx;
+  a.counts = in->counts;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.y = y;
+  return hip_status(twell::launch_hidden_down(a, s));
 }
 
 // The forward up to twell::kFewRows rows: the small-batch gate spills the z
@@ -624,6 +678,65 @@ int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16
                           reinterpret_cast<float*>(base + L.spill), reinterpret_cast<float*>(base + L.part), s);
 }
 
+int twell_gateup_pack(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, int64_t M, int64_t d,
+                      int64_t F, int32_t T, int32_t C, const twell_packed* out, float* z_debug, float* h_debug,
+                      void* ctrl, size_t ctrl_bytes_, void* stream) {
+  if ((M != 0 && !x) || !Wg || !WuT || !packed_ok(out, M)) return TWELL_E_INVALID_ARG;
+  if ((z_debug == nullptr) != (h_debug == nullptr)) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
+  if (st != TWELL_OK) return st;
+  return gateup_impl(x, Wg, WuT, M, d, F, T, C, out, z_debug, h_debug, static_cast<uint32_t*>(ctrl),
+                     static_cast<hipStream_t>(stream));
+}
+
+int twell_hidden_down(const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d, int64_t F, int32_t T,
+                      int32_t C, float* y, void* stream) {
+  if (!Wd || !in) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!y || !in->vals || !in->idx || !in->counts)) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK && !twell::sliced_supports(d, F)) st = TWELL_E_UNSUPPORTED;
+  if (st != TWELL_OK) return st;
+  return hidden_down_impl(Wd, in, M, d, F, T, C, y, static_cast<hipStream_t>(stream));
+}
+
+int twell_ffn_forward_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                             int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl,
+                             size_t ctrl_bytes_, void* workspace, size_t ws_bytes, void* stream) {
+  if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
+  if (st == TWELL_OK && !twell::sliced_supports(d, F)) st = TWELL_E_UNSUPPORTED;
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD_GATEUP, M, F, T, C, workspace, ws_bytes);
+  if (st != TWELL_OK) return st;
+  if (M == 0) return TWELL_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(TWELL_OP_FFN_FORWARD_GATEUP, M, F, T, C);
+  const twell_packed p = packed_in_ws(workspace, L);
+  int dev = -1;
+  if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* ss = nullptr;
+  st = side_stream_locked(dev, &ss);
+  if (st != TWELL_OK) return st;
+  st = gateup_impl(x, Wg, WuT, M, d, F, T, C, &p, nullptr, nullptr, static_cast<uint32_t*>(ctrl), s);
+  if (st != TWELL_OK) return st;
+  if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+    return TWELL_E_HIP;
+  const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
+                               at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
+                               fallback_counters(ctrl, M), ss->s);
+  const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
+  st = hidden_down_impl(Wd, &p, M, d, F, T, C, y, s);
+  if (!joined || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return TWELL_E_HIP;
+  return st != TWELL_OK ? st : st_fb;
+}
+
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
                             void* workspace, size_t ws_bytes, void* stream) {
@@ -684,9 +797,10 @@ int twell_gather_rows(const uint16_t* W, int64_t F, int64_t d, const int32_t* sr
 size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
   if (check_dims(M, d, F) != TWELL_OK) return 0;
   if (op == TWELL_OP_GATE_PACK || op == TWELL_OP_FFN_FORWARD || op == TWELL_OP_SLICED_UPDOWN ||
-      op == TWELL_OP_COLUMN_ACTIVITY) {
+      op == TWELL_OP_COLUMN_ACTIVITY || op == TWELL_OP_FFN_FORWARD_GATEUP) {
     if (check_tc(F, T, C) != TWELL_OK) return 0;
-    if (op == TWELL_OP_SLICED_UPDOWN && !twell::sliced_supports(d, F)) return 0;
+    if ((op == TWELL_OP_SLICED_UPDOWN || op == TWELL_OP_FFN_FORWARD_GATEUP) && !twell::sliced_supports(d, F))
+      return 0;
   } else if (op == TWELL_OP_DENSE_FFN || op == TWELL_OP_DENSE_FALLBACK) {
     if (F % 64 != 0) return 0;
     T = 0;

@@ -28,6 +28,10 @@ struct GateArgs {
   float* z_debug;   // nullable
   uint32_t* col_active;  // nullable: bit j % 32 of word j / 32 ORed with "some row has z_j > 0"
   float* spill;          // nullable, small-batch kernel only: [M, F/T, T] raw z of every (row, tile) with count > C
+  // Gate-only variant (gateup_pack): the up weights, and an optional [M, F]
+  // dump of the hidden values h = ReLU(z) u (z goes to z_debug).
+  const uint16_t* WuT = nullptr;
+  float* h_debug = nullptr;
 };
 
 struct FusedArgs {
@@ -147,6 +151,10 @@ hipError_t launch_gather_rows(const uint16_t* W, int F, int d, const int32_t* sr
                               hipStream_t s);
 
 hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
+// Gate-only variant: dense gate and up products with the packing of h in the
+// epilogue (vals hold h), then the down product from that packing.
+hipError_t launch_gateup_pack(const GateArgs& a, hipStream_t s);
+hipError_t launch_hidden_down(const SlicedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);
 

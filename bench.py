@@ -95,7 +95,8 @@ def parse():
     ap.add_argument("--workload", default="ffn1p5b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU oracle sample")
-    ap.add_argument("--only", choices=["forward", "gate", "fused", "sliced", "fallback", "dense", "copy", "backward"],
+    ap.add_argument("--only", choices=["forward", "gate", "fused", "sliced", "fallback", "dense", "copy", "backward",
+                                       "gateup"],
                     default=None,
                     help="run only this leg (for profiler runs); prints a short line")
     ap.add_argument("--copy-mb", type=int, default=1024, help="size of the calibration copy (--only copy)")
@@ -198,9 +199,10 @@ def dense_torch(x, Wg, WuT, Wd):
     return run
 
 
-def layer_sweep(dev, names, steps, warmup, graphs=False):
-    """Sparse forward vs the dense baselines on each named layer; with
-    `graphs`, every leg is timed by HIP graph replay (graph_time)."""
+def layer_sweep(dev, names, steps, warmup, graphs=False, with_gateup=False):
+    """Sparse forward vs the dense baselines on each named layer (and, with
+    `with_gateup`, the gate-only variant); with `graphs`, every leg is timed
+    by HIP graph replay (graph_time)."""
     import numpy as np
     import torch
 
@@ -219,8 +221,14 @@ def layer_sweep(dev, names, steps, warmup, graphs=False):
         fwd = lambda: tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws, ctrl=ctrl)  # noqa: E731
         dense = lambda: tw.dense_ffn_forward(x, Wg, WuT, Wd, y=y, workspace=wsd)  # noqa: E731
         dt = dense_torch(x, Wg, WuT, Wd)
+        legs = [("sparse", fwd, y), ("dense", dense, y), ("dense_hipblaslt", dt, None)]
+        gateup_ok = with_gateup and tw.workspace_bytes(tw.OP_FFN_FORWARD_GATEUP, w.M, w.d, w.F, w.T, w.C) > 0
+        if gateup_ok:  # the gate-only variant (dense gate and up products, sparse down)
+            wsg = tw.Workspace(dev)
+            gu = lambda: tw.ffn_forward_gateup(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=wsg, ctrl=ctrl)  # noqa: E731
+            legs.append(("sparse_gateup", gu, y))
         res, replay_ok = {}, {}
-        for key, fn, o in (("sparse", fwd, y), ("dense", dense, y), ("dense_hipblaslt", dt, None)):
+        for key, fn, o in legs:
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
@@ -240,6 +248,10 @@ def layer_sweep(dev, names, steps, warmup, graphs=False):
             "speedup_vs_dense": round(res["dense"] / res["sparse"], 3),
             "speedup_vs_dense_hipblaslt": round(res["dense_hipblaslt"] / res["sparse"], 3),
         })
+        if gateup_ok:
+            out[-1]["gateup_ms"] = round(res["sparse_gateup"], 5)
+            out[-1]["gateup_speedup_vs_dense_hipblaslt"] = round(res["dense_hipblaslt"] / res["sparse_gateup"], 3)
+            out[-1]["gateup_speedup_vs_sparse"] = round(res["sparse"] / res["sparse_gateup"], 3)
         if graphs:
             out[-1]["timing"] = "hip_graph"
             out[-1]["graph_replays_match_eager"] = replay_ok
@@ -665,8 +677,10 @@ def main():
             dst = torch.empty_like(src)
             fn = lambda: torch.mul(src, 2.0, out=dst)  # noqa: E731
         else:
+            ws_gu = tw.Workspace(dev)
+            gateup = lambda: tw.ffn_forward_gateup(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_gu)  # noqa: E731
             fn = {"forward": fwd, "gate": gate, "fused": fused, "sliced": sliced, "dense": dense,
-                  "fallback": fallback}[args.only]
+                  "fallback": fallback, "gateup": gateup}[args.only]
             gate()  # the fused leg reads a packing
         for _ in range(args.warmup):
             fn()
@@ -729,7 +743,7 @@ def main():
         from synth import WORKLOADS as _W
 
         sweep = sorted((k for k in _W if k.startswith("sweep_")), key=lambda k: _W[k].mean_nnz)
-        out["density_sweep"] = layer_sweep(dev, sweep, args.sweep_steps, 2)
+        out["density_sweep"] = layer_sweep(dev, sweep, args.sweep_steps, 2, with_gateup=True)
         decode = sorted((k for k in _W if k.startswith("decode_")), key=lambda k: _W[k].M)
         out["decode_batches"] = layer_sweep(dev, decode, 4 * args.sweep_steps, 4, graphs=True)
         out["dead_unit_compaction"] = dead_unit_compaction(dev, "ffn1p5b_heavytail", 2 * args.sweep_steps, 3)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 5
+#define TWELL_ABI_VERSION 6
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -73,6 +73,7 @@ extern "C" {
 #define TWELL_OP_DENSE_FALLBACK 3
 #define TWELL_OP_SLICED_UPDOWN 4
 #define TWELL_OP_COLUMN_ACTIVITY 5
+#define TWELL_OP_FFN_FORWARD_GATEUP 6
 
 /* TwELL packing of ReLU(x Wg^T) with tile width T and capacity C
  * (the format: tgviewer.app Telegram post, part "Вот тут и решает TwELL";
@@ -201,6 +202,45 @@ int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ gate-only variant
+ * A variant of the forward that the pages do not describe, for densities
+ * where gathering one WuT row per stored unit costs more than a dense up
+ * product: the gate and up products are dense (one MFMA kernel reading one x
+ * tile for both) and the TwELL packing holds the hidden value
+ * h = ReLU(z) * u; only the down product gathers, one Wd row per stored unit.
+ * The active set is still the gate's (z > 0; the gate decides which units
+ * are live: Tencent Cloud article, section 1), so counts, slots, tile-local
+ * indices and the overflow set are those twell_gate_pack gives; a stored h
+ * may be zero or negative. Overflow rows take the dense fallback. */
+
+/* Dense gate and up products with h packed in its epilogue: `out` as for
+ * twell_gate_pack except that vals hold h (fp32, from fp32 z and u).
+ * z_debug, h_debug: both NULL, or both [M, F] fp32 receiving every z and
+ * every h = ReLU(z) u (for bit-exact checks of the packing).
+ * ctrl: >= twell_ctrl_bytes(M). */
+int twell_gateup_pack(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, int64_t M, int64_t d,
+                      int64_t F, int32_t T, int32_t C, const twell_packed* out, float* z_debug,
+                      float* h_debug, void* ctrl, size_t ctrl_bytes, void* stream);
+
+/* Down product from a packing of h (twell_gateup_pack): for every row that is
+ * not an overflow row, y[r] = sum over stored units j of h_j * Wd[j] in fp32;
+ * overflow rows of y are not written. Gathers d / 8 columns of Wd per XCD,
+ * as twell_sliced_updown does; d and F as for that call. */
+int twell_hidden_down(const uint16_t* Wd, const twell_packed* in, int64_t M, int64_t d, int64_t F,
+                      int32_t T, int32_t C, float* y, void* stream);
+
+/* The whole gate-only forward: twell_gateup_pack, then twell_hidden_down on
+ * `stream` and the dense fallback of overflow rows on the side stream (as in
+ * twell_ffn_forward); y [M, d] fp32 fully written. The packing sits at the
+ * start of the workspace, where twell_packed_view finds it given a workspace
+ * of twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...) bytes.
+ * ctrl: >= twell_ctrl_bytes(M); workspace: >=
+ * twell_workspace_bytes(TWELL_OP_FFN_FORWARD_GATEUP, ...). */
+int twell_ffn_forward_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T,
+                             int32_t C, float* y, void* ctrl, size_t ctrl_bytes, void* workspace,
+                             size_t ws_bytes, void* stream);
 
 /* Dead gate units (pulsen.vercel.app article, dead-neuron paragraph: at the
  * recommended L1 coefficient over 30% of the units are never active; Tencent

@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 5
+    assert L.twell_abi_version() == 6
     for s in (OK, E_ARG, E_UNSUP, E_WS, -4, -5):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"

@@ -565,3 +565,97 @@ def test_training_edge_cases():
     assert int(hyz.count.sum().item()) == 0
     for t in tw.ffn_backward(xpos, Wneg, WuT, Wd, dy, hyz):
         assert torch.count_nonzero(t).item() == 0
+
+
+# ------------------------------------------------------------ gate-only variant
+GATEUP_SMALL = ["tiny", "uniform_ragged", "heavytail_small", "zipf_small", "t64_odd_tiles", "dense11_small",
+                "long_rows", "few_rows_d768", "few_rows_cut_spill", "d2048_small"]
+
+
+def run_gateup(inp, debug=True):
+    w = inp.workload
+    x, Wg, WuT, _ = dev(inp)
+    z = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV) if debug else None
+    h = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV) if debug else None
+    p = tw.gateup_pack(x, Wg, WuT, w.T, w.C, z_debug=z, h_debug=h)
+    torch.cuda.synchronize()
+    return p, (z.cpu().numpy() if debug else None), (h.cpu().numpy() if debug else None)
+
+
+@pytest.mark.parametrize("name", GATEUP_SMALL)
+def test_gateup_packing_bitexact(name):
+    """Packing of h against the oracle fed the kernel's own z and h, bit for
+    bit; the debug-free instance gives the same bits; z and h agree with the
+    fp64 definition (checks the two MFMA products and their layout)."""
+    inp, Z, rms, _ = small_case(name)
+    w = inp.workload
+    p, z, h = run_gateup(inp)
+    assert np.abs(z - Z).max() <= 1e-4 * rms.max()
+    U = O.up_projections(inp.x, inp.WuT)
+    H = np.maximum(Z, 0) * U
+    act = z > 0
+    assert np.abs(h[act] - (np.maximum(z, 0) * U)[act]).max() <= 1e-4 * max(np.abs(H).max(), 1e-30)
+    ref = O.pack_twell_hidden(z, h, w.T, w.C)
+    check_packing_bitexact(host_packing(p), ref)
+    p2, _, _ = run_gateup(inp, debug=False)
+    check_packing_bitexact(host_packing(p2), ref)
+    # z is summed in the same k order as in the gate kernel, so the counts,
+    # indices and overflow set are that kernel's; the active sets against fp64 z
+    g = host_packing(tw.gate_pack(*dev(inp)[:2], w.T, w.C))
+    assert np.array_equal(g["counts"], ref.counts) and np.array_equal(g["ovf"], ref.ovf)
+    check_active_set(dict(counts=ref.counts, idx=ref.idx, vals=O.pack_twell(z, w.T, w.C).vals), Z, rms, w.T, w.C)
+
+
+@pytest.mark.parametrize("name", GATEUP_SMALL)
+def test_gateup_forward_matches_definition(name):
+    """The gate-only forward against the fp64 definition over the whole
+    tensor; gateup_pack + hidden_down + dense_fallback give its bits, and
+    hidden_down leaves overflow rows untouched."""
+    inp, _, _, Y = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    y = tw.ffn_forward_gateup(x, Wg, WuT, Wd, w.T, w.C, y=nan_y(w.M, w.d))
+    yh = y.cpu().numpy()
+    rel, mx = check_y(yh, Y)
+    p = tw.gateup_pack(x, Wg, WuT, w.T, w.C)
+    g = host_packing(p)
+    yc = tw.hidden_down(Wd, p, nan_y(w.M, w.d))
+    yc_h = yc.cpu().numpy()
+    fit = np.setdiff1d(np.arange(w.M), g["ovf"])
+    assert np.isnan(yc_h[g["ovf"]]).all() and np.isfinite(yc_h[fit]).all()
+    tw.dense_fallback(x, Wg, WuT, Wd, p, yc)
+    assert np.array_equal(yc.cpu().numpy().view(np.uint32), yh.view(np.uint32))
+    print(f"{name}: gate-only forward rel L2 {rel:.2e}, overflow rows {g['n_ovf']}")
+
+
+def test_gateup_unsupported_d():
+    inp, _, _, _ = small_case("fused_only_d2304")
+    w = inp.workload
+    with pytest.raises(tw.TwellError) as e:
+        tw.ffn_forward_gateup(*dev(inp), w.T, w.C)
+    assert e.value.status == -2
+
+
+@pytest.mark.parametrize("name", ["ffn1p5b", "sweep_p1pct", "sweep_p3pct", "sweep_p11pct"])
+def test_gateup_full_size(name):
+    """The gate-only forward at full size: packing bit-exact against the
+    oracle on the kernel's z and h, y over the whole tensor against the fp64
+    definition."""
+    inp = make_inputs(WORKLOADS[name])
+    w = inp.workload
+    print(f"[gateup-full] {name} M={w.M} d={w.d} F={w.F} T={w.T} C={w.C}", flush=True)
+    x, Wg, WuT, Wd = dev(inp)
+    ws = tw.Workspace(DEV)
+    y = tw.ffn_forward_gateup(x, Wg, WuT, Wd, w.T, w.C, y=nan_y(w.M, w.d), workspace=ws)
+    view = host_packing(tw.packed_view(w.M, w.d, w.F, w.T, w.C, workspace=ws, device=DEV))
+    yh = y.cpu().numpy()
+    assert np.isfinite(yh).all()
+    p, z, h = run_gateup(inp)
+    ref = O.pack_twell_hidden(z, h, w.T, w.C)
+    del z, h
+    check_packing_bitexact(host_packing(p), ref)
+    check_packing_bitexact(view, ref)
+    del ref
+    Y = _chunked(lambda r: O.dense_gated_ffn(inp.x, inp.Wg, inp.WuT, inp.Wd, rows=r), w.M)
+    rel, mx = check_y(yh, Y)
+    print(f"[gateup-full] {name}: overflow rows {view['n_ovf']}, whole-tensor rel L2 {rel:.2e}", flush=True)
