@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     Hybrid,
     Packed,
+    Spill,
     TwellError,
     Workspace,
     column_activity,
@@ -30,6 +31,7 @@ from ._lib import (  # noqa: F401
     ffn_forward_gateup,
     fused_updown,
     gate_pack,
+    gate_pack_spill,
     gateup_pack,
     gather_rows,
     header_functions,

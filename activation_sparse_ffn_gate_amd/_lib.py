@@ -49,9 +49,19 @@ class _Hybrid(ctypes.Structure):
     ]
 
 
+class _Spill(ctypes.Structure):
+    _fields_ = [
+        ("z", ctypes.c_void_p),
+        ("slot", ctypes.c_void_p),
+        ("n_spill", ctypes.c_void_p),
+        ("cap", ctypes.c_int64),
+    ]
+
+
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _PK = ctypes.POINTER(_Packed)
 _PH = ctypes.POINTER(_Hybrid)
+_PS = ctypes.POINTER(_Spill)
 _SIGNATURES = {
     "twell_gate_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _SZ, _P]),
     "twell_fused_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
@@ -67,7 +77,8 @@ _SIGNATURES = {
     "twell_column_activity": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_live_layout": (ctypes.c_int, [_P, _I64, _I32, _P, _I64, ctypes.POINTER(_I64)]),
     "twell_gather_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
-    "twell_hybrid_pack": (ctypes.c_int, [_PK, _I64, _I64, _I32, _I32, _I32, _I64, _PH, _P]),
+    "twell_hybrid_pack": (ctypes.c_int, [_PK, _PS, _I64, _I64, _I32, _I32, _I32, _I64, _PH, _P]),
+    "twell_gate_pack_spill": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _PS, _P, _P, _SZ, _P]),
     "twell_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32, _I64]),
     "twell_ffn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _PH, _I64, _I64, _I64, _I32, _I64, _P, _P, _P, _P,
                                           _P, _SZ, _P]),
@@ -472,12 +483,60 @@ class Hybrid:
                                                         self.res_vals, self.n_res)))
 
 
-def hybrid_pack(packed: Packed, F: int, K: int, R: int, out: Hybrid | None = None) -> Hybrid:
-    """twell_hybrid_pack: the hybrid format from a packing with C == T."""
+@dataclass
+class Spill:
+    """Device tensors of a training gate's spill list (see twell_spill in include/twell.h)."""
+
+    z: "object"  # float32 [cap, T]
+    slot: "object"  # int32 [M, F/T]
+    n_spill: "object"  # int32 [1]
+
+    @classmethod
+    def empty(cls, M, F, T, cap, device):
+        torch = _torch()
+        return cls(torch.empty((max(cap, 1), T), dtype=torch.float32, device=device),
+                   torch.empty((M, F // T), dtype=torch.int32, device=device),
+                   torch.empty((1,), dtype=torch.int32, device=device))
+
+    @property
+    def cap(self) -> int:
+        return int(self.z.shape[0])
+
+    def _c(self) -> _Spill:
+        return _Spill(_dptr(self.z).value or 0, _dptr(self.slot).value or 0, _dptr(self.n_spill).value or 0,
+                      self.cap)
+
+
+def gate_pack_spill(x, Wg, T: int, C: int, cap: int, out: Packed | None = None, spill: Spill | None = None,
+                    z_debug=None, ctrl=None):
+    """twell_gate_pack_spill: the training gate (packing of capacity C plus the
+    spill list of tiles over C, `cap` records). Returns (Packed, Spill)."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    px, pw = _bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d))
+    out = out or Packed.empty(M, F, T, C, x.device)
+    spill = spill or Spill.empty(M, F, T, cap, x.device)
+    pz = ctypes.c_void_p(0)
+    if z_debug is not None:
+        _f32_out(z_debug, "z_debug", (M, F), x.device)
+        pz = _dptr(z_debug)
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    pk, sp = out._c(), spill._c()
+    _check(lib().twell_gate_pack_spill(px, pw, M, d, F, T, C, ctypes.byref(pk), ctypes.byref(sp), pz, cp, cn,
+                                       _stream(x)), "twell_gate_pack_spill")
+    return out, spill
+
+
+def hybrid_pack(packed: Packed, F: int, K: int, R: int, out: Hybrid | None = None,
+                spill: Spill | None = None) -> Hybrid:
+    """twell_hybrid_pack: the hybrid format from a packing (C == T), or from a
+    packing of smaller C and the spill list of the same training gate."""
     M = packed.counts.shape[0]
     out = out or Hybrid.empty(M, F, K, R, packed.counts.device)
     pk, ph = packed._c(), out._c()
-    _check(lib().twell_hybrid_pack(ctypes.byref(pk), M, F, packed.T, packed.C, K, R, ctypes.byref(ph),
+    sp = ctypes.byref(spill._c()) if spill is not None else None
+    _check(lib().twell_hybrid_pack(ctypes.byref(pk), sp, M, F, packed.T, packed.C, K, R, ctypes.byref(ph),
                                    _stream(packed.counts)), "twell_hybrid_pack")
     return out
 

@@ -15,9 +15,11 @@
 // rows (per unit).
 //
 // MI355X mapping.
-//  * hybrid_pack: one wave per row turns a complete TwELL packing (C = T, so
-//    no tile drops units) into the row's block (global unit indices,
-//    ascending) or, past K, a reserve row.
+//  * hybrid_pack: one wave per row turns a TwELL packing into the row's
+//    block (global unit indices, ascending) or, past K active units, a
+//    reserve row. Tiles within capacity C come from the packing's slots; with
+//    C < T a tile over C comes from the training gate's spill record (every z
+//    of that tile), so no active unit is lost.
 //  * row_backward: one wave per token, x and dy rows in registers, the dx row
 //    accumulated in fp32; per listed unit three coalesced 2d-byte row gathers
 //    (WuT_j gives u and the du term, Wd_j gives dh, Wg_j the dz term), two
@@ -53,6 +55,14 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void hybrid_pack_kernel(HybridArgs
   total = __builtin_amdgcn_readlane(wave_inclusive_scan(total), 63);
   if (lane == 0) a.h_count[r] = total;
   const size_t slot0 = static_cast<size_t>(r) * nT * a.C;
+  // A tile with more than C active units (only when C < T) is read from its
+  // spill record: all T pre-activations, the active ones (z > 0) in ascending
+  // order. A record past the list's capacity was not stored: the tile then
+  // reads as empty (the caller sees n_spill > capacity).
+  auto record = [&](int t) -> const float* {
+    const int rec = a.rec_slot[static_cast<size_t>(r) * nT + t];
+    return (rec >= 0 && rec < a.rec_cap) ? a.rec_z + static_cast<size_t>(rec) * a.T : nullptr;
+  };
   if (total <= a.K) {
     int32_t* bi = a.h_idx + static_cast<size_t>(r) * a.K;
     float* bv = a.h_vals + static_cast<size_t>(r) * a.K;
@@ -62,10 +72,22 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void hybrid_pack_kernel(HybridArgs
       const int c = t < nT ? static_cast<int>(cnt[t]) : 0;
       const int incl = wave_inclusive_scan(c);
       const int off = base + incl - c;
-      for (int s = 0; s < c; ++s) {
-        const size_t k = slot0 + static_cast<size_t>(t) * a.C + s;
-        bi[off + s] = t * a.T + static_cast<int>(a.idx[k]);
-        bv[off + s] = a.vals[k];
+      if (c <= a.C) {
+        for (int s = 0; s < c; ++s) {
+          const size_t k = slot0 + static_cast<size_t>(t) * a.C + s;
+          bi[off + s] = t * a.T + static_cast<int>(a.idx[k]);
+          bv[off + s] = a.vals[k];
+        }
+      } else if (const float* z = record(t)) {
+        int s = 0;
+        for (int i = 0; i < a.T && s < c; ++i) {
+          const float v = z[i];
+          if (v > 0.f) {
+            bi[off + s] = t * a.T + i;
+            bv[off + s] = v;
+            ++s;
+          }
+        }
       }
       base += __builtin_amdgcn_readlane(incl, 63);
     }
@@ -85,9 +107,16 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void hybrid_pack_kernel(HybridArgs
   __threadfence();  // the zeros are in place before the values go over them
   for (int t = lane; t < nT; t += 64) {
     const int c = cnt[t];
-    for (int s = 0; s < c; ++s) {
-      const size_t k = slot0 + static_cast<size_t>(t) * a.C + s;
-      dense[t * a.T + static_cast<int>(a.idx[k])] = a.vals[k];
+    if (c <= a.C) {
+      for (int s = 0; s < c; ++s) {
+        const size_t k = slot0 + static_cast<size_t>(t) * a.C + s;
+        dense[t * a.T + static_cast<int>(a.idx[k])] = a.vals[k];
+      }
+    } else if (const float* z = record(t)) {
+      for (int i = 0; i < a.T; ++i) {
+        const float v = z[i];
+        if (v > 0.f) dense[t * a.T + i] = v;
+      }
     }
   }
 }

@@ -8,6 +8,7 @@
 // before every call and left zero after it:
 //   word 0 (64-bit): low half = rows appended so far, high half = workgroups
 //                    finished;
+//   word 2: spill records taken (training gate only);
 //   then one dedup flag per row.
 // Appends and arrivals use the one 64-bit word, so the workgroup that arrives
 // last learns from its own arrival both that it is last and how many rows were
@@ -65,6 +66,12 @@ __device__ __forceinline__ void overflow_finalize(const GateArgs& a, int appende
   }
   if (threadIdx.x == 0) {
     *a.n_ovf = static_cast<int32_t>(n);
+    if (a.rec_n != nullptr) {  // spill records: publish the count, clear the counter
+      if (n == 0) __threadfence();  // (no fence was taken above)
+      uint32_t* rc = a.ctrl + 2;
+      *a.rec_n = static_cast<int32_t>(__hip_atomic_load(rc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      __hip_atomic_store(rc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __hip_atomic_store(word, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

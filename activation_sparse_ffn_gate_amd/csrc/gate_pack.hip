@@ -42,7 +42,7 @@ constexpr int kTileBytes = 256 * kBK * 2;  // one operand tile of a stage (16 KB
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kDmaPerStage = 8;  // global_load_lds per thread per stage (4 for A, 4 for B)
 
-template <int kT, bool kDebug, bool kAct>
+template <int kT, bool kDebug, bool kAct, bool kSpill = false>
 __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m, int tiles_n) {
   // One LDS object only: with a second one the compiler attaches alias scopes
   // to LDS accesses and then makes every LDS read wait for all outstanding
@@ -239,6 +239,7 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
   for (int tt = 0; tt < kTilesPerWave; ++tt) cnt[tt][0] = cnt[tt][1] = 0;
 
   uint64_t act[4] = {0, 0, 0, 0};  // column activity (kAct): OR of the ballots
+  int spilled = 0;                 // kSpill: this thread wrote spill records
 
   static_for<0, 64>([&](auto g) {
     constexpr int mb = decltype(g)::value / 16, v = decltype(g)::value % 16;
@@ -270,6 +271,29 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
       // Whether every active unit of both tokens fits in the C slots.
       const bool fits = p_lo[kBlocksPerTile] <= static_cast<uint32_t>(C) &&
                         p_hi[kBlocksPerTile] <= static_cast<uint32_t>(C);
+      if constexpr (kSpill) {
+        // Every z of an overflowing (token, tile) goes to a spill record: lane
+        // 0 (token of lanes 0-31) and lane 32 take the records with a vector
+        // atomic, then each half writes its token's T values.
+        if (!fits) {
+          const bool ov_lo = p_lo[kBlocksPerTile] > static_cast<uint32_t>(C);
+          const bool ov_hi = p_hi[kBlocksPerTile] > static_cast<uint32_t>(C);
+          int rec = 0;
+          if ((lane == 0 && ov_lo) || (lane == 32 && ov_hi)) rec = atomicAdd(reinterpret_cast<int*>(a.ctrl + 2), 1);
+          const int rec_me = half ? __builtin_amdgcn_readlane(rec, 32) : __builtin_amdgcn_readlane(rec, 0);
+          if (half ? ov_hi : ov_lo) {
+            // the slot map names the record even past the list's capacity, so
+            // readers see that it was not stored
+            if (col == 0) a.rec_slot[static_cast<size_t>(row) * nT + tile] = rec_me;
+            if (rec_me < a.rec_cap) {
+              float* rz = a.rec_z + static_cast<size_t>(rec_me) * kT;
+#pragma unroll
+              for (int q = 0; q < kBlocksPerTile; ++q) rz[q * 32 + col] = acc[mb][tt * kBlocksPerTile + q][v];
+            }
+          }
+          spilled = 1;
+        }
+      }
       const uint32_t base = row * row_slots + static_cast<uint32_t>(tile * C);
 #pragma unroll
       for (int q = 0; q < kBlocksPerTile; ++q) {
@@ -321,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 
   // The last workgroup publishes n_ovf and clears the control block; the
   // stage buffers are idle now and hold its flag.
-  overflow_finalize(a, appended, reinterpret_cast<int*>(smem));
+  overflow_finalize(a, appended | spilled, reinterpret_cast<int*>(smem));
 }
 
 __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }
@@ -329,12 +353,24 @@ __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }
 }  // namespace
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
-  if (a.M <= kSkinnyMaxM) return launch_gate_pack_skinny(a, s);
-  if (a.spill != nullptr) return hipErrorInvalidValue;  // only the small-batch kernel spills
+  const bool rec = a.rec_z != nullptr;  // spill records: the large kernel at every M
+  if (a.M <= kSkinnyMaxM && !rec) return launch_gate_pack_skinny(a, s);
+  if (a.spill != nullptr) return hipErrorInvalidValue;  // only the small-batch kernel spills whole rows
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles_n = (a.F + kBN - 1) / kBN;
   const dim3 grid(tiles_m * tiles_n), block(256);
   const bool dbg = a.z_debug != nullptr, act = a.col_active != nullptr;
+  if (rec) {
+    if (act || a.rec_slot == nullptr || a.rec_n == nullptr) return hipErrorInvalidValue;
+    if (a.T == 128) {
+      if (dbg) gate_pack_kernel<128, true, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+      else gate_pack_kernel<128, false, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    } else {
+      if (dbg) gate_pack_kernel<64, true, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+      else gate_pack_kernel<64, false, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
+    }
+    return hipGetLastError();
+  }
   if (a.T == 128) {
     if (dbg) gate_pack_kernel<128, true, false><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);
     else if (act) gate_pack_kernel<128, false, true><<<grid, block, 0, s>>>(a, tiles_m, tiles_n);

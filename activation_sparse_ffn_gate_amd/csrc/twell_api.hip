@@ -467,13 +467,15 @@ BwdLayout bwd_layout(int64_t M, int64_t F, int32_t K, int64_t R) {
 
 extern "C" {
 
-int twell_hybrid_pack(const twell_packed* in, int64_t M, int64_t F, int32_t T, int32_t C, int32_t K,
-                      int64_t R, const twell_hybrid* out, void* stream) {
+int twell_hybrid_pack(const twell_packed* in, const twell_spill* spill, int64_t M, int64_t F, int32_t T,
+                      int32_t C, int32_t K, int64_t R, const twell_hybrid* out, void* stream) {
   if (!in || !out || !out->n_res) return TWELL_E_INVALID_ARG;
   if (M < 0 || M > kMaxM || F <= 0 || F > kMaxF || K < 1 || R < 0 || R > M) return TWELL_E_INVALID_ARG;
   int st = check_tc(F, T, C);
   if (st != TWELL_OK) return st;
-  if (C != T) return TWELL_E_UNSUPPORTED;  // the packing must hold every active unit
+  // below C = T the tiles that overflow come from the spill list
+  if (C != T && (!spill || !spill->z || !spill->slot || spill->cap < 0 || spill->cap * T >= (int64_t(1) << 31)))
+    return TWELL_E_INVALID_ARG;
   if (M != 0 && (!in->vals || !in->idx || !in->counts || !out->idx || !out->vals || !out->count))
     return TWELL_E_INVALID_ARG;
   if (R != 0 && (!out->res_rows || !out->res_vals)) return TWELL_E_INVALID_ARG;
@@ -493,9 +495,54 @@ int twell_hybrid_pack(const twell_packed* in, int64_t M, int64_t F, int32_t T, i
   a.res_rows = out->res_rows;
   a.res_vals = out->res_vals;
   a.n_res = out->n_res;
+  if (C != T) {
+    a.rec_z = spill->z;
+    a.rec_slot = spill->slot;
+    a.rec_cap = int(spill->cap);
+  }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (M == 0) return hip_status(twell::launch_set_i32(out->n_res, 0, s));
   return hip_status(twell::launch_hybrid_pack(a, s));
+}
+
+int twell_gate_pack_spill(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F, int32_t T,
+                          int32_t C, const twell_packed* out, const twell_spill* spill, float* z_debug,
+                          void* ctrl, size_t ctrl_bytes_, void* stream) {
+  if ((M != 0 && !x) || !Wg || !packed_ok(out, M) || !spill || !spill->n_spill) return TWELL_E_INVALID_ARG;
+  if (M != 0 && (!spill->slot || !spill->z)) return TWELL_E_INVALID_ARG;
+  if (spill->cap < 0 || spill->cap * T >= (int64_t(1) << 31)) return TWELL_E_INVALID_ARG;
+  int st = check_dims(M, d, F);
+  if (st == TWELL_OK) st = check_tc(F, T, C);
+  if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
+  if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
+  if (st != TWELL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    st = hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
+    return st != TWELL_OK ? st : hip_status(twell::launch_set_i32(spill->n_spill, 0, s));
+  }
+  twell::GateArgs a;
+  a.x = x;
+  a.Wg = Wg;
+  a.M = int(M);
+  a.d = int(d);
+  a.F = int(F);
+  a.T = T;
+  a.C = C;
+  a.vals = out->vals;
+  a.idx = out->idx;
+  a.counts = out->counts;
+  a.ovf_rows = out->ovf_rows;
+  a.n_ovf = out->n_ovf;
+  a.ctrl = static_cast<uint32_t*>(ctrl);
+  a.z_debug = z_debug;
+  a.col_active = nullptr;
+  a.spill = nullptr;
+  a.rec_z = spill->z;
+  a.rec_slot = spill->slot;
+  a.rec_n = spill->n_spill;
+  a.rec_cap = int(spill->cap);
+  return hip_status(twell::launch_gate_pack(a, s));
 }
 
 size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {

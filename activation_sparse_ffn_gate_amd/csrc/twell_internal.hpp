@@ -32,6 +32,14 @@ struct GateArgs {
   // dump of the hidden values h = ReLU(z) u (z goes to z_debug).
   const uint16_t* WuT = nullptr;
   float* h_debug = nullptr;
+  // Training gate (large kernel only): every z of each (row, tile) whose count
+  // exceeds C goes to a record of a list of rec_cap records of T floats;
+  // rec_slot[row][tile] receives its record, rec_n the records needed (the
+  // counter lives in ctrl word 2 and is cleared by the last workgroup).
+  float* rec_z = nullptr;
+  int32_t* rec_slot = nullptr;
+  int32_t* rec_n = nullptr;
+  int rec_cap = 0;
 };
 
 struct FusedArgs {
@@ -119,6 +127,10 @@ struct HybridArgs {
   int32_t* res_rows;  // [R]
   float* res_vals;    // [R, F]
   int32_t* n_res;     // [1]
+  // C < T: the spill records of the overflowing tiles (GateArgs::rec_*)
+  const float* rec_z = nullptr;
+  const int32_t* rec_slot = nullptr;
+  int rec_cap = 0;
 };
 hipError_t launch_hybrid_pack(const HybridArgs& a, hipStream_t s);
 

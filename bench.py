@@ -288,8 +288,28 @@ def dense_backward_torch(x, Wg, WuT, Wd, dy):
     return run
 
 
+def dense_forward_torch_train(x, Wg, WuT, Wd):
+    """The dense gated FFN's training forward on hipBLASLt through torch: z|u
+    in one GEMM (kept for the backward), h = ReLU(z) u, y = h Wd."""
+    import torch
+
+    F = Wg.shape[0]
+    Wgu = torch.cat([Wg, WuT], 0).contiguous()
+
+    def run():
+        zu = torch.nn.functional.linear(x, Wgu)
+        h = torch.relu(zu[:, :F]) * zu[:, F:]
+        return zu, h @ Wd
+
+    return run
+
+
 def training_backward(dev, name, K, R, steps, warmup):
-    """Hybrid pack and sparse backward against the dense backward (hipBLASLt)."""
+    """The training path of one layer: the training gate (packing of capacity
+    C plus the spill list of tiles over C), the forward's up/down and fallback
+    from that packing (y), the hybrid format and the sparse backward; against
+    the dense path on hipBLASLt (forward keeping z and u, backward). Also the
+    bytes each path keeps for the backward and holds in between."""
     import numpy as np
     import torch
 
@@ -302,30 +322,81 @@ def training_backward(dev, name, K, R, steps, warmup):
     x, Wg, WuT, Wd = (td(a) for a in (inp.x, inp.Wg, inp.WuT, inp.Wd))
     dy = td(make_upstream_grad(w))
     stream = torch.cuda.current_stream(dev)
-    p = tw.gate_pack(x, Wg, w.T, w.T)  # C = T: every active unit kept
+    nT = w.F // w.T
+    cap = max(1024, w.M * nT // 16)  # spill records (tiles over C) the list holds
+    p, sp = tw.gate_pack_spill(x, Wg, w.T, w.C, cap)
     hy = tw.Hybrid.empty(w.M, w.F, K, R, dev)
-    ws = tw.Workspace(dev)
+    ws, ws_s, ws_f = tw.Workspace(dev), tw.Workspace(dev), tw.Workspace(dev)
+    y = torch.empty((w.M, w.d), dtype=torch.float32, device=dev)
     outs = (torch.empty((w.M, w.d), dtype=torch.float32, device=dev),
             *(torch.empty((w.F, w.d), dtype=torch.float32, device=dev) for _ in range(3)))
-    pack = lambda: tw.hybrid_pack(p, w.F, K, R, out=hy)  # noqa: E731
+    sliced_ok = tw.workspace_bytes(tw.OP_SLICED_UPDOWN, w.M, w.d, w.F, w.T, w.C) > 0
+    gate = lambda: tw.gate_pack_spill(x, Wg, w.T, w.C, cap, out=p, spill=sp)  # noqa: E731
+
+    def updown():
+        if sliced_ok:
+            tw.sliced_updown(x, WuT, Wd, p, y=y, workspace=ws_s)
+        else:
+            tw.fused_updown(x, WuT, Wd, p, y=y)
+        tw.dense_fallback(x, Wg, WuT, Wd, p, y, workspace=ws_f)
+
+    pack = lambda: tw.hybrid_pack(p, w.F, K, R, out=hy, spill=sp)  # noqa: E731
     bwd = lambda: tw.ffn_backward(x, Wg, WuT, Wd, dy, hy, workspace=ws, out=outs)  # noqa: E731
-    dense = dense_backward_torch(x, Wg, WuT, Wd, dy)
+
+    def sparse_step():
+        gate()
+        updown()
+        pack()
+        bwd()
+
+    dense_fwd = dense_forward_torch_train(x, Wg, WuT, Wd)
+    dense_bwd = dense_backward_torch(x, Wg, WuT, Wd, dy)
+
+    def dense_step():
+        dense_fwd()
+        dense_bwd()
+
+    # the former route: a C = T packing (every unit in its slots), no spill list
+    p_ct = tw.Packed.empty(w.M, w.F, w.T, w.T, dev)
+    hy_ct = tw.Hybrid.empty(w.M, w.F, K, R, dev)
+    gate_ct = lambda: tw.gate_pack(x, Wg, w.T, w.T, out=p_ct)  # noqa: E731
+    pack_ct = lambda: tw.hybrid_pack(p_ct, w.F, K, R, out=hy_ct)  # noqa: E731
     res = {}
-    for key, fn in (("hybrid_pack", pack), ("sparse_backward", bwd), ("dense_backward_hipblaslt", dense)):
+    for key, fn in (("gate_spill", gate), ("forward_updown_fallback", updown), ("hybrid_pack", pack),
+                    ("sparse_backward", bwd), ("sparse_training_step", sparse_step),
+                    ("dense_forward_hipblaslt", dense_fwd), ("dense_backward_hipblaslt", dense_bwd),
+                    ("dense_training_step_hipblaslt", dense_step), ("gate_c_eq_t", gate_ct),
+                    ("hybrid_pack_c_eq_t", pack_ct)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         res[key] = time_loop(fn, steps, stream)
-    pack()
+    sparse_step()
     torch.cuda.synchronize()
     count = hy.count.cpu().numpy()
     flops_dense = 12.0 * w.M * w.d * w.F
-    out = {"workload": name, "M": w.M, "d": w.d, "F": w.F, "K": K, "R": R,
+    nbytes = lambda *ts: int(sum(t.numel() * t.element_size() for t in ts))  # noqa: E731
+    mem = {
+        # kept from the forward for the backward (x and the weights are common to both)
+        "dense_saved_bytes": w.M * 2 * w.F * 2,  # z and u in bf16
+        "sparse_saved_bytes": nbytes(hy.idx, hy.vals, hy.count, hy.res_rows, hy.res_vals, hy.n_res),
+        # held between the gate and the hybrid format
+        "sparse_packing_and_spill_bytes": nbytes(p.vals, p.idx, p.counts, p.ovf_rows, p.n_ovf, sp.z, sp.slot,
+                                                 sp.n_spill),
+        "c_eq_t_packing_bytes": nbytes(p_ct.vals, p_ct.idx, p_ct.counts, p_ct.ovf_rows, p_ct.n_ovf),
+    }
+    mem["sparse_peak_bytes"] = mem["sparse_saved_bytes"] + mem["sparse_packing_and_spill_bytes"]
+    mem["sparse_vs_dense_saved"] = round(mem["sparse_saved_bytes"] / mem["dense_saved_bytes"], 4)
+    mem["sparse_peak_vs_dense_saved"] = round(mem["sparse_peak_bytes"] / mem["dense_saved_bytes"], 4)
+    out = {"workload": name, "M": w.M, "d": w.d, "F": w.F, "T": w.T, "C": w.C, "K": K, "R": R,
+           "spill_cap": cap, "spilled_tiles": int(sp.n_spill.item()),
            "reserve_rows": int(hy.n_res.item()), "entries": int(count.sum()),
-           "dense_backward_tflops": round(flops_dense / (res["dense_backward_hipblaslt"] * 1e-3) / 1e12, 1)}
+           "dense_backward_tflops": round(flops_dense / (res["dense_backward_hipblaslt"] * 1e-3) / 1e12, 1),
+           "memory": mem}
     out.update({f"{k}_ms": round(v, 5) for k, v in res.items()})
-    out["speedup_vs_dense"] = round(res["dense_backward_hipblaslt"] / res["sparse_backward"], 3)
-    del x, Wg, WuT, Wd, dy, p, hy, ws, outs, dense
+    out["speedup_backward_vs_dense"] = round(res["dense_backward_hipblaslt"] / res["sparse_backward"], 3)
+    out["speedup_training_step_vs_dense"] = round(res["dense_training_step_hipblaslt"] / res["sparse_training_step"], 3)
+    del x, Wg, WuT, Wd, dy, p, sp, hy, ws, ws_s, ws_f, outs, y, dense_fwd, dense_bwd, p_ct, hy_ct
     torch.cuda.empty_cache()
     return out
 
@@ -657,8 +728,8 @@ def main():
         from synth import make_upstream_grad
 
         dy = td(make_upstream_grad(w))
-        p_full = tw.gate_pack(x, Wg, w.T, w.T)
-        hy = tw.hybrid_pack(p_full, w.F, 64, min(512, w.M))
+        p_tr, sp_tr = tw.gate_pack_spill(x, Wg, w.T, w.C, max(1024, w.M * (w.F // w.T) // 16))
+        hy = tw.hybrid_pack(p_tr, w.F, 64, min(512, w.M), spill=sp_tr)
         ws_b = tw.Workspace(dev)
         outs = (torch.empty((w.M, w.d), dtype=torch.float32, device=dev),
                 *(torch.empty((w.F, w.d), dtype=torch.float32, device=dev) for _ in range(3)))

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 6
+#define TWELL_ABI_VERSION 7
 
 /* Status codes. */
 #define TWELL_OK 0
@@ -302,10 +302,40 @@ typedef struct twell_hybrid {
   int32_t* n_res;
 } twell_hybrid;
 
-/* The hybrid format from a TwELL packing that holds every active unit:
- * C must equal T (then no tile count exceeds C). K >= 1; 0 <= R <= M. */
-int twell_hybrid_pack(const twell_packed* in, int64_t M, int64_t F, int32_t T, int32_t C, int32_t K,
-                      int64_t R, const twell_hybrid* out, void* stream);
+/* Spill list of the training gate: every pre-activation z of each (row,
+ * tile) whose count exceeds C, so that a packing of small capacity C still
+ * loses no active unit (the hybrid format needs them all) without the
+ * M * F * 5 bytes of a C = T packing.
+ *   z       [cap, T] fp32  record k: the T values z of one (row, tile)
+ *   slot    [M, F/T] int32 record of (row, tile) where counts[row][tile] > C;
+ *                          other entries are not written
+ *   n_spill [1]      int32 records needed; when it exceeds cap the records
+ *                          past cap were not stored and the list is incomplete
+ *   cap              records z holds (0 <= cap < 2^31 / T); z and slot are
+ *                    non-NULL whenever M > 0 */
+typedef struct twell_spill {
+  float* z;
+  int32_t* slot;
+  int32_t* n_spill;
+  int64_t cap;
+} twell_spill;
+
+/* The gate of the training path: twell_gate_pack's output (any C), plus the
+ * spill list of the tiles that overflow C. The kernel is twell_gate_pack's
+ * large-batch one at every M (above 256 rows its packing and z are the same
+ * bits). z_debug: optional [M, F] fp32 receiving every z, as in
+ * twell_gate_pack. ctrl: >= twell_ctrl_bytes(M). */
+int twell_gate_pack_spill(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,
+                          int32_t T, int32_t C, const twell_packed* out, const twell_spill* spill,
+                          float* z_debug, void* ctrl, size_t ctrl_bytes, void* stream);
+
+/* The hybrid format from a TwELL packing and, for C < T, the spill list of
+ * the same call of twell_gate_pack_spill (tiles over C are read from their
+ * records); with C == T no tile overflows and spill may be NULL. K >= 1;
+ * 0 <= R <= M. The format is valid when *n_res <= R and, with a spill list,
+ * *n_spill <= its cap. */
+int twell_hybrid_pack(const twell_packed* in, const twell_spill* spill, int64_t M, int64_t F, int32_t T,
+                      int32_t C, int32_t K, int64_t R, const twell_hybrid* out, void* stream);
 
 /* Workspace bytes of twell_ffn_backward (0 for invalid arguments). */
 size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R);

@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = tw.lib()
-    assert L.twell_abi_version() == 6
+    assert L.twell_abi_version() == 7
     for s in (OK, E_ARG, E_UNSUP, E_WS, -4, -5):
         assert tw.status_string(s)
     assert tw.status_string(12345) == "unknown status"
@@ -208,7 +208,7 @@ def test_column_activity_and_gather_validation():
 
 # ------------------------------------------------------------ training side
 def test_backward_validation():
-    from activation_sparse_ffn_gate_amd._lib import _Hybrid
+    from activation_sparse_ffn_gate_amd._lib import _Hybrid, _Spill
 
     L = tw.lib()
     M, d, F, T, K, R = 64, 256, 1024, 64, 8, 4
@@ -222,10 +222,22 @@ def test_backward_validation():
     pk = _Packed(FAKE.value, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
     hy = _Hybrid(*([FAKE.value] * 6))
     hp = L.twell_hybrid_pack
-    assert hp(ctypes.byref(pk), M, F, T, 8, K, R, ctypes.byref(hy), None) == E_UNSUP  # C != T drops units
-    assert hp(ctypes.byref(pk), M, F, T, T, 0, R, ctypes.byref(hy), None) == E_ARG
-    assert hp(ctypes.byref(pk), M, F, T, T, K, M + 1, ctypes.byref(hy), None) == E_ARG
-    assert hp(None, M, F, T, T, K, R, ctypes.byref(hy), None) == E_ARG
+    assert hp(ctypes.byref(pk), None, M, F, T, 8, K, R, ctypes.byref(hy), None) == E_ARG  # C < T needs the spill
+    sp = _Spill(FAKE.value, FAKE.value, FAKE.value, -1)
+    assert hp(ctypes.byref(pk), ctypes.byref(sp), M, F, T, 8, K, R, ctypes.byref(hy), None) == E_ARG  # cap < 0
+    assert hp(ctypes.byref(pk), None, M, F, T, T, 0, R, ctypes.byref(hy), None) == E_ARG
+    assert hp(ctypes.byref(pk), None, M, F, T, T, K, M + 1, ctypes.byref(hy), None) == E_ARG
+    assert hp(None, None, M, F, T, T, K, R, ctypes.byref(hy), None) == E_ARG
+    gs = L.twell_gate_pack_spill
+    g = tw.ctrl_bytes(M)
+    ok_sp = _Spill(FAKE.value, FAKE.value, FAKE.value, 16)
+    assert gs(FAKE, FAKE, M, d, F, T, 8, ctypes.byref(pk), None, None, FAKE, g, None) == E_ARG
+    no_n = _Spill(FAKE.value, FAKE.value, 0, 16)
+    assert gs(FAKE, FAKE, M, d, F, T, 8, ctypes.byref(pk), ctypes.byref(no_n), None, FAKE, g, None) == E_ARG
+    big = _Spill(FAKE.value, FAKE.value, FAKE.value, (1 << 31) // T)
+    assert gs(FAKE, FAKE, M, d, F, T, 8, ctypes.byref(pk), ctypes.byref(big), None, FAKE, g, None) == E_ARG
+    assert gs(FAKE, FAKE, M, d, F, 96, 8, ctypes.byref(pk), ctypes.byref(ok_sp), None, FAKE, g, None) == E_UNSUP
+    assert gs(FAKE, FAKE, M, d, F, T, 8, ctypes.byref(pk), ctypes.byref(ok_sp), None, FAKE, g - 256, None) == E_WS
     fb = L.twell_ffn_backward
     ok = [FAKE] * 5 + [ctypes.byref(hy), M, d, F, K, R] + [FAKE] * 4
     assert fb(*ok, FAKE, ws - 256, None) == E_WS

@@ -314,12 +314,8 @@ def train_case(name):
     return inp, z32, O.hybrid_pack(z32, K), hy, make_upstream_grad(w)
 
 
-@pytest.mark.parametrize("name", list(TRAIN))
-def test_hybrid_pack(name):
-    """Hybrid format against the oracle's on the kernel's own z: bit-exact."""
-    inp, z32, ref, hy, _ = train_case(name)
-    w = inp.workload
-    K, R = TRAIN[name]
+def check_hybrid(hy, ref, K, R):
+    """A device hybrid format against the oracle's, bit for bit."""
     count = hy.count.cpu().numpy()
     assert np.array_equal(count, ref.count)
     idx, vals = hy.idx.cpu().numpy(), hy.vals.cpu().numpy()
@@ -336,6 +332,16 @@ def test_hybrid_pack(name):
     assert np.array_equal(dense[order].view(np.uint32), ref.res_vals.view(np.uint32))
     for i, r in enumerate(rows):  # a reserve row's block names its slot
         assert idx[r, 0] == i
+    return count, n_res
+
+
+@pytest.mark.parametrize("name", list(TRAIN))
+def test_hybrid_pack(name):
+    """Hybrid format against the oracle's on the kernel's own z: bit-exact."""
+    inp, z32, ref, hy, _ = train_case(name)
+    w = inp.workload
+    K, R = TRAIN[name]
+    count, n_res = check_hybrid(hy, ref, K, R)
     print(f"{name}: K={K}, reserve rows {n_res} of {w.M}, mean count {count.mean():.1f}")
 
 
@@ -659,3 +665,104 @@ def test_gateup_full_size(name):
     Y = _chunked(lambda r: O.dense_gated_ffn(inp.x, inp.Wg, inp.WuT, inp.Wd, rows=r), w.M)
     rel, mx = check_y(yh, Y)
     print(f"[gateup-full] {name}: overflow rows {view['n_ovf']}, whole-tensor rel L2 {rel:.2e}", flush=True)
+
+
+# ------------------------------------------- training gate with spill records
+# (case, K, R) with C < T: tiles over C reach the hybrid format through the
+# spill list instead of a C = T packing.
+SPILL_TRAIN = {
+    "tiny": (48, 64),
+    "uniform_ragged": (8, 300),
+    "heavytail_small": (40, 1100),
+    "zipf_small": (16, 520),
+    "dense11_small": (40, 257),
+    "few_rows_cut_spill": (600, 24),
+}
+
+
+def run_gate_spill(inp, cap=None):
+    w = inp.workload
+    x, Wg, _, _ = dev(inp)
+    nT = w.F // w.T
+    cap = w.M * nT if cap is None else cap
+    z = torch.empty((w.M, w.F), dtype=torch.float32, device=DEV)
+    p, sp = tw.gate_pack_spill(x, Wg, w.T, w.C, cap, z_debug=z)
+    torch.cuda.synchronize()
+    return p, sp, z.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(SPILL_TRAIN))
+def test_gate_spill_records(name):
+    """The training gate: packing bit-exact against the oracle on its own z;
+    one spill record per (row, tile) over C holding that tile's z bits; with
+    a list too short the count still covers every tile."""
+    inp, _, _, _ = small_case(name)
+    w = inp.workload
+    nT = w.F // w.T
+    p, sp, z32 = run_gate_spill(inp)
+    ref = O.pack_twell(z32, w.T, w.C)
+    check_packing_bitexact(host_packing(p), ref)
+    over = ref.counts.astype(np.int64) > w.C
+    n = int(sp.n_spill.item())
+    assert n == int(over.sum())
+    slots = sp.slot.cpu().numpy()[over]
+    assert np.array_equal(np.sort(slots), np.arange(n))
+    recs = sp.z.cpu().numpy()[slots]
+    assert np.array_equal(recs.view(np.uint32), z32.reshape(w.M, nT, w.T)[over].view(np.uint32))
+    if w.M > 256:  # the forward's gate kernel gives the same bits
+        g = host_packing(tw.gate_pack(*dev(inp)[:2], w.T, w.C))
+        check_packing_bitexact(g, ref)
+    if n > 1:  # half the records: the rest are not stored, n_spill says so
+        _, sp2, _ = run_gate_spill(inp, cap=n // 2)
+        assert int(sp2.n_spill.item()) == n
+    print(f"{name}: {n} spilled tiles of {w.M * nT}")
+
+
+@pytest.mark.parametrize("name", list(SPILL_TRAIN))
+def test_hybrid_from_spill(name):
+    """The hybrid format from a C < T packing and its spill list equals the
+    oracle's on the gate's z, bit for bit, and the backward over it matches
+    the oracle on the same active set."""
+    inp, _, _, _ = small_case(name)
+    w = inp.workload
+    K, R = SPILL_TRAIN[name]
+    p, sp, z32 = run_gate_spill(inp)
+    hy = tw.hybrid_pack(p, w.F, K, R, spill=sp)
+    ref = O.hybrid_pack(z32, K)
+    count, n_res = check_hybrid(hy, ref, K, R)
+    x, Wg, WuT, Wd = dev(inp)
+    dy_bits = make_upstream_grad(w)
+    got = [t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, to_device(dy_bits, DEV), hy)]
+    want = O.ffn_backward_from_hybrid(ref, inp.x, inp.Wg, inp.WuT, inp.Wd, dy_bits)
+    for label, g, a in zip(("dx", "dWg", "dWuT", "dWd"), got, want):
+        rel, _ = check_y(g, a)
+    print(f"{name}: K={K}, C={w.C}, spilled {int(sp.n_spill.item())}, reserve rows {n_res}")
+
+
+def test_training_spill_full_size():
+    """Heavy-tailed layer at full size (C = 16, K = 64, R = 512): the hybrid
+    format from the spill list is the C = T route's, bit for bit, and so are
+    the gradients."""
+    w = WORKLOADS["ffn1p5b_heavytail"]
+    inp = make_inputs(w)
+    K, R = 64, 512
+    x, Wg, WuT, Wd = dev(inp)
+    dy = to_device(make_upstream_grad(w), DEV)
+    p, sp = tw.gate_pack_spill(x, Wg, w.T, w.C, 16384)
+    hy = tw.hybrid_pack(p, w.F, K, R, spill=sp)
+    n = int(sp.n_spill.item())
+    assert 0 < n <= 16384
+    full = tw.hybrid_pack(tw.gate_pack(x, Wg, w.T, w.T), w.F, K, R)
+    for a, b in ((hy.count, full.count), (hy.n_res, full.n_res)):
+        assert torch.equal(a, b)
+    count = hy.count.cpu().numpy()
+    fit = count <= K
+    for a, b in ((hy.idx, full.idx), (hy.vals, full.vals)):
+        ah, bh = a.cpu().numpy(), b.cpu().numpy()
+        for r in np.flatnonzero(fit):
+            assert np.array_equal(ah[r, :count[r]].view(np.uint32), bh[r, :count[r]].view(np.uint32))
+    g1 = [t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, dy, hy)]
+    g2 = [t.cpu().numpy() for t in tw.ffn_backward(x, Wg, WuT, Wd, dy, full)]
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    print(f"[train-spill] spilled tiles {n}, reserve rows {int(hy.n_res.item())}")
