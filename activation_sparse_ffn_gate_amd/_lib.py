@@ -101,6 +101,14 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is missing: build it with `python -m activation_sparse_ffn_gate_amd._build` "
                 "(there is no CPU fallback)"
             )
+        # torch ships its own HIP runtime under the same soname as the system
+        # one that libtwell.so links to; the first one loaded serves the whole
+        # process, and torch's streams are only valid in torch's. So torch is
+        # loaded first, and libtwell.so then binds to the same runtime.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)
