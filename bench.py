@@ -66,19 +66,27 @@ def _counter_kib(path, counter, kernel=None):
 
 def record_traffic(root, workload):
     """Write profiles/traffic.json from rocprofv3 --pmc runs stored under root:
-    pmc_<leg>_fetch / pmc_<leg>_write for leg in gate, fused, sliced and copy
-    (the sliced leg holds both of its kernels; their traffic is summed)."""
+    pmc_<workload>_<leg>_fetch / _write for leg in gate, fused and sliced (the
+    sliced leg holds both of its kernels; their traffic is summed), scaled by
+    pmc_copy_fetch / pmc_copy_write of a plain copy of known size. Workloads
+    already recorded from the same kernel sources are kept."""
     cf = COPY_BYTES / 1024.0 / _counter_kib(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE")
     cw = COPY_BYTES / 1024.0 / _counter_kib(os.path.join(root, "pmc_copy_write"), "WRITE_SIZE")
     rec = {"sources_sha256": sources_hash(), "calibration": {"fetch_factor": cf, "write_factor": cw,
                                                              "copy_bytes": COPY_BYTES}, "workloads": {}}
+    if os.path.exists(TRAFFIC_FILE):  # keep other workloads recorded from the same sources
+        with open(TRAFFIC_FILE) as f:
+            old = json.load(f)
+        if old.get("sources_sha256") == rec["sources_sha256"]:
+            rec["workloads"] = old.get("workloads", {})
     ent = {}
     for leg, name, kernels in (("gate", "gate_pack", ["gate_pack"]), ("fused", "fused_updown", ["fused_updown"]),
                                ("sliced", "sliced_updown", ["sliced_up_kernel", "sliced_down_kernel"])):
-        if not os.path.isdir(os.path.join(root, f"pmc_{leg}_fetch")):
+        d_f = os.path.join(root, f"pmc_{workload}_{leg}_fetch")
+        if not os.path.isdir(d_f):
             continue
-        fk = sum(_counter_kib(os.path.join(root, f"pmc_{leg}_fetch"), "FETCH_SIZE", k) for k in kernels)
-        wk = sum(_counter_kib(os.path.join(root, f"pmc_{leg}_write"), "WRITE_SIZE", k) for k in kernels)
+        fk = sum(_counter_kib(d_f, "FETCH_SIZE", k) for k in kernels)
+        wk = sum(_counter_kib(os.path.join(root, f"pmc_{workload}_{leg}_write"), "WRITE_SIZE", k) for k in kernels)
         ent[name] = {"fetch_kib_raw": fk, "write_kib_raw": wk,
                      "traffic_bytes": fk * 1024.0 * cf + wk * 1024.0 * cw}
     rec["workloads"][workload] = ent
