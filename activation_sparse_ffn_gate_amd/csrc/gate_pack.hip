@@ -12,15 +12,20 @@
 // chunks through a 5-stage LDS ring filled by gfx950's global_load_lds (16
 // bytes per lane straight into LDS, no register staging), issued four chunks
 // ahead so HBM/MALL latency hides behind the MFMAs. Small batches use
-// gate_pack_skinny.hip instead (see launch_gate_pack). Each wave's 128 units are
-// whole TwELL tiles (T = 128 or 64), so every (token, tile) segment lives in
-// one wave and the packing needs no LDS round trip: in the accumulator layout
-// one register holds, across the 64 lanes, 32 consecutive units of two tokens,
-// so a 64-bit ballot of (z > 0) gives both tokens' activity masks; popcounts of
-// the masks give the per-tile count and each lane's slot is the popcount of
-// the mask bits below it (ascending unit order). Values (fp32) and tile-local
-// indices are stored only for slots < C; the per-(token, tile) count is stored
-// unclamped.
+// gate_pack_skinny.hip instead (see launch_gate_pack).
+//
+// Packing. The forward's instance stages the finished tile through the idle
+// LDS ring, 128 token rows at a time: the two waves that own those rows write
+// their accumulators, then every thread takes one (token, 128 units) segment
+// and builds its activity mask with plain compares (unit c at bit c), so the
+// per-tile count is a popcount and the stored slots are the first C set bits
+// in ascending unit order, each found with a count-trailing-zeros. Only slots
+// < C are stored (fp32 value, tile-local index); the count is stored
+// unclamped. The debug, column-activity and spill instances pack straight from
+// the accumulators instead: in the MFMA layout one register holds, across the
+// 64 lanes, 32 consecutive units of two tokens, so a 64-bit ballot of (z > 0)
+// gives both tokens' masks and a lane's slot is the popcount of the mask bits
+// below it. Both forms produce the same bits; the tests compare them.
 //
 // Overflow rows (some tile count > C) are appended to a deduplicated list with
 // device-scope atomics. The last workgroup to finish publishes the list length
@@ -41,6 +46,13 @@ constexpr int kAhead = kStages - 1;  // chunks in flight ahead of the one comput
 constexpr int kTileBytes = 256 * kBK * 2;  // one operand tile of a stage (16 KB)
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kDmaPerStage = 8;  // global_load_lds per thread per stage (4 for A, 4 for B)
+
+// m * 2 + (z > 0): the compare sets VCC per lane (strict: +0, -0 and NaN
+// give 0) and an add with carry-in shifts that bit in.
+__device__ __forceinline__ uint32_t shift_in_active(uint32_t m, float z) {
+  asm("v_cmp_lt_f32_e32 vcc, 0, %1\n\tv_addc_co_u32_e32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(z) : "vcc");
+  return m;
+}
 
 template <int kT, bool kDebug, bool kAct, bool kSpill = false>
 __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles_m, int tiles_n) {
@@ -231,6 +243,92 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb][v] = ok ? acc[mb][nb][v] : 0.f;
       }
+  }
+
+  if constexpr (!kAct && !kSpill) {
+    // Packing through LDS. The ring is idle after the K loop; each of two
+    // passes holds the 128 token rows of one half of the tile (row-major, rows
+    // padded by 4 floats so the column reads below fall in distinct banks).
+    // Every thread then packs one (token, 128 units) on its own: a 128-bit
+    // activity mask from plain compares, its popcounts, and the first C
+    // active units in ascending order. No cross-lane or scalar step.
+    constexpr int kZS = kBN + 4;
+    constexpr int kTilesPerThread = 128 / kT;
+    constexpr int kWordsPerTile = kT / 32;
+    float* zs = reinterpret_cast<float*>(smem);
+    // the low 32 bits of an LDS object's generic address are its LDS offset
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    const int t = threadIdx.x;
+    const int r_loc = t & 127, th = t >> 7;
+    int appended = 0;
+    waitcnt<63, 0>();
+    raw_barrier();  // every wave is past its last fragment reads of the ring
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
+        // ds_write_b32 straight from the accumulator registers, at immediate
+        // offsets from two bases (rows 0-63 and 64-127 of the pass), so no
+        // copies and no address arithmetic per value.
+        const uint32_t b0 = lds_base + static_cast<uint32_t>((acc_row(0, half) * kZS + wn * 128 + col) * 4);
+        const uint32_t b1 = b0 + 64u * kZS * 4u;
+        static_for<0, 256>([&](auto I) {
+          constexpr int mb = I.value / 64, nb = (I.value / 16) % 4, v = I.value % 16;
+          constexpr int off = (((mb & 1) * 32 + 8 * (v / 4) + (v % 4)) * kZS + nb * 32) * 4;
+          static_assert(off < 65536, "ds offset");
+          const uint32_t base = mb < 2 ? b0 : b1;
+          const float val = acc[mb][nb][v];
+          asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(base), "a"(val), "i"(off) : "memory");
+        });
+      }
+      waitcnt<63, 0>();
+      raw_barrier();  // the pass's rows are in LDS
+      const float* zr = zs + r_loc * kZS + th * 128;
+      uint32_t m[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // shift-in from the highest unit down: unit c ends at bit c
+        uint32_t mw = 0;
+#pragma unroll
+        for (int q = 7; q >= 0; --q) {
+          const float4 z4 = *reinterpret_cast<const float4*>(zr + w * 32 + 4 * q);
+          mw = shift_in_active(mw, z4.w);
+          mw = shift_in_active(mw, z4.z);
+          mw = shift_in_active(mw, z4.y);
+          mw = shift_in_active(mw, z4.x);
+        }
+        m[w] = mw;
+      }
+      const int token = m0 + pass * 128 + r_loc;
+#pragma unroll
+      for (int k = 0; k < kTilesPerThread; ++k) {
+        const int tile = (n0 + th * 128) / kT + k;
+        if (token < a.M && tile < nT) {
+          int cnt = 0;
+#pragma unroll
+          for (int w = 0; w < kWordsPerTile; ++w) cnt += __popc(m[k * kWordsPerTile + w]);
+          a.counts[static_cast<size_t>(token) * nT + tile] = static_cast<uint16_t>(cnt);
+          if (cnt > C) appended |= overflow_append(a, token);
+          const uint32_t base = static_cast<uint32_t>(token) * row_slots + static_cast<uint32_t>(tile * C);
+          int slot = 0;
+#pragma unroll
+          for (int w = 0; w < kWordsPerTile; ++w) {
+            uint32_t mask = m[k * kWordsPerTile + w];
+            while (mask != 0u && slot < C) {
+              const int b = __builtin_ctz(mask);
+              const int c = w * 32 + b;  // tile-local unit
+              store_at(a.vals, (base + slot) * 4u, zr[k * kT + c]);
+              store_at(a.idx, base + slot, static_cast<uint8_t>(c));
+              ++slot;
+              mask &= mask - 1u;
+            }
+          }
+        }
+      }
+      waitcnt<63, 0>();
+      raw_barrier();  // every thread is done reading before the next pass writes
+    }
+    overflow_finalize(a, appended, reinterpret_cast<int*>(smem));
+    return;
   }
 
   // cnt[tt][h] of lane L = count of token wrow0 + 64 h + L in TwELL tile tile0 + tt
