@@ -16,17 +16,23 @@
 // become L2 hits.
 //
 // The price is one exchange between the slices, since u_j needs all d
-// columns. Two launches:
-//   up:   wave per (row, slice s): part[s][r][e] = g_e * (x_r[s] . WuT[j_e][s])
-//         for the e-th stored unit of the row (tile-major, slot order);
+// columns. Three launches:
+//   lists: wave per row: the row's TwELL tiles become one contiguous list of
+//         (unit j_e, gate value g_e) entries in (tile, slot) order, and its
+//         length n (-1 for an overflow row). The packing is read once per row
+//         here, not once per slice: a sparse row touches a cache line of
+//         values in most of its tiles, so reading it in every slice's pass
+//         was the largest share of the up pass's traffic.
+//   up:   wave per (row, slice s): part[s][r][e] = g_e * (x_r[s] . WuT[j_e][s]);
 //   down: wave per (row, slice s): h_e = sum over s' of part[s'][r][e] in the
 //         fixed order s' = 0..7, y_r[s] = sum_e h_e * Wd[j_e][s].
 // So a stored unit's hidden value does pass through memory: 8 fp32 partials per
 // stored unit (the dense hidden matrix is still never formed). part is laid
-// out [8][M][nT * C] so each row's partials of a slice are contiguous. The up
-// pass also leaves each row's unit list (units [M][nT * C]) and its length
-// (row_len [M], -1 for an overflow row), so the down pass starts from those
-// instead of re-reading counts and indices.
+// out [8][M][nT * C] so each row's partials of a slice are contiguous; the
+// list is [M][nT * C] entries of 8 bytes. Every list and partial read starts
+// at a fixed offset of its row, so a wave issues the row's length, its first
+// 64 entries and its x slice together, and the weight gathers are its second
+// round trip.
 //
 // Lane layout. A slice is d / 8 bf16 = d / 64 sixteen-byte pieces. A row of a
 // slice is read by a group of L lanes (L = the largest power of two <= 64
@@ -138,44 +144,69 @@ __device__ __forceinline__ int stage_row(const SlicedArgs& a, int row, const int
   return ebase;
 }
 
+// Row lists: one wave per row, four rows a workgroup. Lane l holds the
+// count of tile t0 + l; a prefix sum over the lanes gives each tile's first
+// entry. A row with a count above C is an overflow row: its length is -1 and
+// the entries it may have written are never read.
+__global__ __launch_bounds__(256) void row_list_kernel(SlicedArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
+  const int nT = a.F / a.T;
+  const int C = a.C;
+  const int tmask = a.T - 1;  // T is a power of two: keeps every unit index < F
+  const size_t cap = static_cast<size_t>(nT) * C;
+  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
+  int2* lrow = a.list + static_cast<size_t>(row) * cap;
+  int base = 0;
+  for (int t0 = 0; t0 < nT; t0 += 64) {
+    const int t = t0 + lane;
+    const int c = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
+    if (__ballot(c > C) != 0) {
+      if (lane == 0) a.row_len[row] = -1;
+      return;
+    }
+    const int incl = wave_inclusive_scan(c);
+    const int o = base + incl - c;
+    const size_t slot0 = (static_cast<size_t>(row) * nT + t) * C;
+    for (int e = 0; e < c; ++e)
+      lrow[o + e] = make_int2(t * a.T + (static_cast<int>(a.idx[slot0 + e]) & tmask),
+                              __float_as_int(a.vals[slot0 + e]));
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (lane == 0) a.row_len[row] = base;
+}
+
+// Entries a wave takes from the row list per round: one per lane.
+constexpr int kRound = 64;
+
 // Waves per SIMD the up pass is compiled for. The kernel waits on dependent
-// global round trips (counts, list, weight rows), so more resident waves hide
-// more of them: at V = 4 (d = 2048), 6 instead of the 4 that its registers
-// would allow was measured 4% faster at M = 4096, F = 8192, at the cost of a
-// small register spill. Other shapes keep the compiler's choice.
+// global round trips (list, weight rows), so more resident waves hide more of
+// them. Shapes other than V = 4 (d = 2048) keep the compiler's choice.
 template <int V>
 constexpr int up_waves_per_simd() {
   return V == 4 ? 6 : 1;
 }
 
 template <int L, int V, int U>
-__global__ __launch_bounds__(64 * kRowsPerWG) __attribute__((amdgpu_waves_per_eu(up_waves_per_simd<V>(), 8)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(up_waves_per_simd<V>(), 8)))
 void sliced_up_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
-  __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
-  __shared__ float s_g[kRowsPerWG][kListCap + kListPad];
+  __shared__ int s_j[kRound + kListPad];
+  __shared__ float s_g[kRound + kListPad];
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int slice = blockIdx.x % kSlices;
-  const int row = (blockIdx.x / kSlices) * kRowsPerWG + w;
+  const int row = blockIdx.x / kSlices;
   if (row >= a.M) return;
 
-  const int nT = a.F / a.T;
-  const uint16_t* cnt_row = a.counts + static_cast<size_t>(row) * nT;
-  int c[kCountGroups];
-  bool over = false;
-#pragma unroll
-  for (int q = 0; q < kCountGroups; ++q) {
-    const int t = q * 64 + lane;
-    c[q] = (t < nT) ? static_cast<int>(cnt_row[t]) : 0;
-    over |= c[q] > a.C;
-  }
-  for (int t = 64 * kCountGroups + lane; t < nT; t += 64) over |= cnt_row[t] > a.C;
-  if (__ballot(over) != 0) {  // owned by the dense fallback
-    if (slice == 0 && lane == 0) a.row_len[row] = -1;
-    return;
-  }
+  const int cap = (a.F / a.T) * a.C;
+  const int2* lrow = a.list + static_cast<size_t>(row) * cap;
+  // First round trip, all issued together: the row's first kRound list
+  // entries (whatever the row holds past its length is dropped below), its
+  // length, and the x slice.
+  int2 ent = (lane < cap) ? lrow[lane] : make_int2(0, 0);
+  const int n = __builtin_amdgcn_readfirstlane(a.row_len[row]);  // -1: overflow row
 
   const int grp = lane / L, li = lane % L;
   const int col0 = slice * (a.d / kSlices) + li * 8;  // piece v of this lane: col0 + v * 8L
@@ -184,28 +215,26 @@ void sliced_up_kernel(SlicedArgs a) {
 #pragma unroll
   for (int v = 0; v < V; ++v) xv[v] = gload16(xr + v * 8 * L);
 
-  const size_t cap = static_cast<size_t>(nT) * a.C;
   float* prow = a.part + (static_cast<size_t>(slice) * a.M + row) * cap;
-  int32_t* urow = a.units + static_cast<size_t>(row) * cap;
-  int* lj = s_j[w];
-  float* lg = s_g[w];
-
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
   const uint32_t col_bytes = static_cast<uint32_t>(col0) * 2u;
-  const int total = stage_row<true>(a, row, c, lj, lg, [&](int n, int e0) {
-    if (slice == 0)  // the row's unit list, for the down pass
-      for (int i = lane; i < n; i += 64) urow[e0 + i] = lj[i];
-    static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the list");
-    if (lane < kListPad) {  // pad to a whole step: unit 0 (a valid row), value 0
-      lj[n + lane] = 0;
-      lg[n + lane] = 0.f;
-    }
+  static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the round");
+  if (lane < kListPad) {  // steps past a round's last entry read unit 0 (a valid row), value 0
+    s_j[kRound + lane] = 0;
+    s_g[kRound + lane] = 0.f;
+  }
+  for (int e0 = 0; e0 < n; e0 += kRound) {
+    const int m = min(kRound, n - e0);
+    int2 nxt = make_int2(0, 0);  // the next round's entries, loaded behind this round's gathers
+    if (e0 + kRound + lane < n) nxt = lrow[e0 + kRound + lane];
+    s_j[lane] = (lane < m) ? ent.x : 0;
+    s_g[lane] = (lane < m) ? __int_as_float(ent.y) : 0.f;
     wave_lds_sync();
-    for (int e = 0; e < n; e += G * U) {
+    for (int e = 0; e < m; e += G * U) {
       u32x4_t wu[U][V];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t off = static_cast<uint32_t>(lj[e + u * G + grp]) * row_bytes + col_bytes;
+        const uint32_t off = static_cast<uint32_t>(s_j[e + u * G + grp]) * row_bytes + col_bytes;
 #pragma unroll
         for (int v = 0; v < V; ++v) wu[u][v] = ldg16(a.WuT, off + v * 16 * L);
       }
@@ -218,40 +247,43 @@ void sliced_up_kernel(SlicedArgs a) {
           for (int q = 0; q < 4; ++q) part = dot2_bf16(xv[v][q], wu[u][v][q], part);
         part = group_sum<L>(part);
         const int k = e + u * G + grp;
-        if (li == 0 && k < n) prow[e0 + k] = lg[k] * part;
+        if (li == 0 && k < m) prow[e0 + k] = s_g[k] * part;
       }
     }
-  });
-  if (slice == 0 && lane == 0) a.row_len[row] = total;
+    wave_lds_sync();
+    ent = nxt;
+  }
 }
 
 // L > 32 (one group, lanes >= L idle) avoids the cross-group sum for the
 // slice widths that are not a power-of-two number of pieces.
 template <int L, int V, int U>
-__global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs a) {
+__global__ __launch_bounds__(64) void sliced_down_kernel(SlicedArgs a) {
   constexpr int G = 64 / L;
-  __shared__ int s_j[kRowsPerWG][kListCap + kListPad];
-  __shared__ float s_h[kRowsPerWG][kListCap + kListPad];
+  __shared__ int s_j[kRound + kListPad];
+  __shared__ float s_h[kRound + kListPad];
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int slice = blockIdx.x % kSlices;
-  const int row = (blockIdx.x / kSlices) * kRowsPerWG + w;
+  const int row = blockIdx.x / kSlices;
   if (row >= a.M) return;
+
+  const int cap = (a.F / a.T) * a.C;
+  const int2* lrow = a.list + static_cast<size_t>(row) * cap;
+  // The row's length and the units of its first kRound entries together; the
+  // empty asm keeps the entry load ahead of the length test.
+  int j = (lane < cap) ? lrow[lane].x : 0;
+  asm volatile("" ::"v"(j));
   const int n = __builtin_amdgcn_readfirstlane(a.row_len[row]);
-  if (n < 0) return;  // overflow row
+  if (n < 0) return;  // overflow row: the dense fallback writes it
 
   const int grp = (G == 1) ? 0 : lane / L;
   const int li = (G == 1) ? min(lane, L - 1) : lane % L;  // idle lanes repeat the last piece
   const int col0 = slice * (a.d / kSlices) + li * 8;
-  const size_t cap = static_cast<size_t>(a.F / a.T) * a.C;
   const size_t slice_stride = static_cast<size_t>(a.M) * cap;
   const float* prow = a.part + static_cast<size_t>(row) * cap;
   const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
   const uint32_t col_bytes = static_cast<uint32_t>(col0) * 2u;
-  const int32_t* urow = a.units + static_cast<size_t>(row) * cap;
-  int* lj = s_j[w];
-  float* lh = s_h[w];
 
   float acc[V][8];
 #pragma unroll
@@ -259,22 +291,23 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[v][k] = 0.f;
 
-  for (int e0 = 0; e0 < n; e0 += kListCap) {
-    const int m = min(kListCap, n - e0);
-    // unit index and h of the staged units: the slices' partial products summed
-    // in slice order
-    for (int i = lane; i < m; i += 64) {
-      lj[i] = urow[e0 + i];
-      float h = 0.f;
+  static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the round");
+  if (lane < kListPad) {  // steps past a round's last entry read unit 0 (a valid row), h 0
+    s_j[kRound + lane] = 0;
+    s_h[kRound + lane] = 0.f;
+  }
+  for (int e0 = 0; e0 < n; e0 += kRound) {
+    const int m = min(kRound, n - e0);
+    int jn = 0;  // the next round's units, loaded behind this round's gathers
+    if (e0 + kRound + lane < n) jn = lrow[e0 + kRound + lane].x;
+    // h of the round's entries: the slices' partial products summed in slice order
+    float h = 0.f;
+    if (lane < m) {
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) h += prow[s * slice_stride + e0 + i];
-      lh[i] = h;
+      for (int s = 0; s < kSlices; ++s) h += prow[s * slice_stride + e0 + lane];
     }
-    static_assert(G * U <= kListPad, "a step reads at most kListPad entries past the list");
-    if (lane < kListPad) {  // pad to a whole step: unit 0 (a valid row), h 0
-      lj[m + lane] = 0;
-      lh[m + lane] = 0.f;
-    }
+    s_j[lane] = (lane < m) ? j : 0;
+    s_h[lane] = h;
     wave_lds_sync();
     for (int e = 0; e < m; e += G * U) {
       u32x4_t wd[U][V];
@@ -282,8 +315,8 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = e + u * G + grp;
-        hv[u] = lh[k];
-        const uint32_t off = static_cast<uint32_t>(lj[k]) * row_bytes + col_bytes;
+        hv[u] = s_h[k];
+        const uint32_t off = static_cast<uint32_t>(s_j[k]) * row_bytes + col_bytes;
 #pragma unroll
         for (int v = 0; v < V; ++v) wd[u][v] = ldg16(a.Wd, off + v * 16 * L);
       }
@@ -298,6 +331,7 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void sliced_down_kernel(SlicedArgs
           }
     }
     wave_lds_sync();
+    j = jn;
   }
 
   // The G groups hold partial sums of the same output columns.
@@ -506,8 +540,8 @@ SlicedLayout sliced_layout(int64_t M, int64_t F, int T, int C) {
   const size_t cap = size_t(F / T) * size_t(C);
   SlicedLayout l;
   l.part = 0;
-  l.units = align256(size_t(kSlices) * size_t(M) * cap * sizeof(float));
-  l.row_len = l.units + align256(size_t(M) * cap * sizeof(int32_t));
+  l.list = align256(size_t(kSlices) * size_t(M) * cap * sizeof(float));
+  l.row_len = l.list + align256(size_t(M) * cap * sizeof(int2));
   l.total = l.row_len + align256(size_t(M) * sizeof(int32_t));
   return l;
 }
@@ -517,8 +551,11 @@ hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s) {
   if (!sliced_supports(a.d, a.F)) return hipErrorInvalidValue;
   lane_split_up(a.d, &Lu, &Vu);
   lane_split_down(a.d, &Ld, &Vd);
-  const dim3 grid(((a.M + kRowsPerWG - 1) / kRowsPerWG) * kSlices), block(64 * kRowsPerWG);
-  hipError_t e = hipErrorInvalidValue;
+  row_list_kernel<<<(a.M + 3) / 4, 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.M * kSlices), block(64);
+  e = hipErrorInvalidValue;
   switch (Lu * 16 + Vu) {
 #define TWELL_CASE(L, V) \
   case L * 16 + V: e = launch_up<L, V>(a, s, grid, block); break;

@@ -216,7 +216,7 @@ int sliced_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, cons
   a.T = T;
   a.C = C;
   a.part = at<float>(region, sl.part);
-  a.units = at<int32_t>(region, sl.units);
+  a.list = at<int2>(region, sl.list);
   a.row_len = at<int32_t>(region, sl.row_len);
   a.y = y;
   return hip_status(twell::launch_sliced_updown(a, s));

@@ -95,14 +95,14 @@ struct SlicedArgs {
   const uint16_t* counts;
   int M, d, F, T, C;
   float* part;       // [kSlices, M, (F / T) * C] partial up-projections
-  int32_t* units;    // [M, (F / T) * C] each row's stored units in (tile, slot) order
+  int2* list;        // [M, (F / T) * C] each row's (unit, gate value bits) in (tile, slot) order
   int32_t* row_len;  // [M] number of stored units, -1 for an overflow row
   float* y;
 };
 
 // Byte offsets of the sliced kernels' buffers inside their workspace region.
 struct SlicedLayout {
-  size_t part, units, row_len, total;
+  size_t part, list, row_len, total;
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
