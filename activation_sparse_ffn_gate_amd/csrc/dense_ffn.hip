@@ -19,10 +19,13 @@
 // K loop (K = F = 8192 for the down product), which would leave most of the GPU
 // idle. Then the K loop of every tile is split S ways (S chosen on the device
 // from the list length): each split stores its fp32 partial tile in the
-// workspace, and the last split of a tile to finish (a per-tile arrival
-// counter in the control block, reset by that last split) adds the S partial
-// tiles in split order and runs the epilogue. The sum order is fixed, so the
-// result does not depend on which split finishes last.
+// workspace and a reduce launch after each product (persistent too, empty when
+// there is no split) adds the S partial tiles in split order and runs the
+// epilogue. The sum order is fixed. The launch boundary makes the partial
+// tiles of every XCD visible to the reducer; an in-kernel last-arriver
+// reduction measured at about half of each product's time (a device-scope
+// fence per split to publish its partial tile, then one workgroup per tile
+// reading all S partial tiles).
 //
 // Workgroup tile 128 x 128, 4 waves as 2 x 2, each wave 64 x 64 (2 x 2 MFMA
 // 32x32x16 blocks), 32-wide K chunks double-buffered in LDS.
@@ -47,7 +50,6 @@ struct SplitPlan {
 };
 
 __device__ __forceinline__ SplitPlan plan_split(bool allowed, int tiles, int nk) {
-  static_assert(kSplitBelow <= kDenseCounters / 2, "one arrival counter per split tile");
   static_assert(2 * kTargetItems <= kDenseSplitSlots, "partial slots of the gated-up kernel");
   if (!allowed || tiles == 0 || tiles >= kSplitBelow) return {1, tiles};
   int S = kTargetItems / tiles;
@@ -56,54 +58,40 @@ __device__ __forceinline__ SplitPlan plan_split(bool allowed, int tiles, int nk)
   return {S, tiles * S};
 }
 
-// Stores this thread's n fp32 accumulators (n / 4 float4) of split slot `slot`.
-template <int N>
-__device__ __forceinline__ void store_partial(float* part, int slot, const float (&v)[N]) {
-  float4* p = reinterpret_cast<float4*>(part) + static_cast<size_t>(slot) * (N / 4) * 256;
-#pragma unroll
-  for (int q = 0; q < N / 4; ++q)
-    p[q * 256 + threadIdx.x] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+// Element (row, column) of float4 q of thread t in a tile's flattened
+// accumulators (flatten below): rows row0 .. row0 + 3 of one column.
+struct PartPos {
+  int row0, col;
+};
+__device__ __forceinline__ PartPos part_pos(int q, int t) {
+  const int w = t >> 6, lane = t & 63;
+  const int k = 4 * q;  // flattened index (i * 2 + j) * 16 + v, v % 4 == 0
+  const int i = k >> 5, j = (k >> 4) & 1, v = k & 15;
+  return {(w >> 1) * 64 + i * 32 + acc_row(v, lane >> 5), (w & 1) * 64 + j * 32 + (lane & 31)};
 }
 
-// v = sum over s = 0 .. S-1 of the partial accumulators stored in slots
-// slot0 + stride * s (this workgroup's own split included), in that order.
-// kPairs loads two slots per round (half the memory round trips, N / 2 more
-// registers).
-template <bool kPairs, int N>
-__device__ __forceinline__ void reduce_partials(const float* part, int slot0, int stride, int S, float (&v)[N]) {
-  const float4* base = reinterpret_cast<const float4*>(part);
-  auto slot_ptr = [&](int s) { return base + static_cast<size_t>(slot0 + stride * s) * (N / 4) * 256 + threadIdx.x; };
+// Stores this thread's 64 fp32 accumulators (16 float4) of split slot `slot`,
+// except float4s whose rows all lie at or past `rows` (tile-local).
+__device__ __forceinline__ void store_partial(float* part, int slot, const float (&v)[64], int rows) {
+  float4* p = reinterpret_cast<float4*>(part) + static_cast<size_t>(slot) * 16 * 256;
 #pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = 0.f;
-  int s = 0;
-  for (; kPairs && s + 2 <= S; s += 2) {
-    const float4* p0 = slot_ptr(s);
-    const float4* p1 = slot_ptr(s + 1);
-    float4 t0[N / 4], t1[N / 4];
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      t0[q] = p0[q * 256];
-      t1[q] = p1[q * 256];
-    }
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      v[4 * q] = (v[4 * q] + t0[q].x) + t1[q].x;
-      v[4 * q + 1] = (v[4 * q + 1] + t0[q].y) + t1[q].y;
-      v[4 * q + 2] = (v[4 * q + 2] + t0[q].z) + t1[q].z;
-      v[4 * q + 3] = (v[4 * q + 3] + t0[q].w) + t1[q].w;
-    }
+  for (int q = 0; q < 16; ++q)
+    if (part_pos(q, threadIdx.x).row0 < rows)
+      p[q * 256 + threadIdx.x] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+// float4 q of thread t summed over slots slot0 + stride * s, s = 0 .. S-1, in that order.
+__device__ __forceinline__ float4 sum_partials(const float* part, int slot0, int stride, int S, int q, int t) {
+  const float4* p = reinterpret_cast<const float4*>(part) + q * 256 + t;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float4 v = p[static_cast<size_t>(slot0 + stride * s) * 16 * 256];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
-  for (; s < S; ++s) {
-    const float4* p0 = slot_ptr(s);
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      const float4 t = p0[q * 256];
-      v[4 * q] += t.x;
-      v[4 * q + 1] += t.y;
-      v[4 * q + 2] += t.z;
-      v[4 * q + 3] += t.w;
-    }
-  }
+  return acc;
 }
 
 // Flattened views of a wave's 2 x 2 block of 32x32 accumulators.
@@ -116,32 +104,6 @@ __device__ __forceinline__ void flatten(const f32x16_t (&acc)[2][2], float (&v)[
       for (int k = 0; k < 16; ++k) v[(i * 2 + j) * 16 + k] = acc[i][j][k];
 }
 
-__device__ __forceinline__ void unflatten(const float (&v)[64], f32x16_t (&acc)[2][2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int k = 0; k < 16; ++k) acc[i][j][k] = v[(i * 2 + j) * 16 + k];
-}
-
-// After a split has stored its partial tile: returns (to every thread of the
-// workgroup) whether it was the tile's last split to arrive. The last one
-// resets the tile's counter and may then read every split's partial tile.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int S, int* s_flag) {
-  __syncthreads();  // every wave's partial stores have completed
-  if (threadIdx.x == 0) {
-    __threadfence();  // ... and are visible to the other XCDs
-    const uint32_t old = atomicAdd(counter, 1u);
-    const bool last = old == static_cast<uint32_t>(S - 1);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __threadfence();  // see the other splits' partial tiles
-  return last;
-}
 
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
@@ -153,11 +115,10 @@ __device__ __forceinline__ f32x16_t zero16() {
 template <bool kGather, bool kSplit>
 __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kTile];
-  __shared__ int s_last;
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
   const int tiles_m = (R + kDM - 1) / kDM;
   const int nk = a.d / kDK;
-  const SplitPlan plan = plan_split(kGather && a.counters != nullptr, tiles_m * tiles_n, nk);
+  const SplitPlan plan = plan_split(kGather && a.split_k, tiles_m * tiles_n, nk);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -238,19 +199,13 @@ __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles
       __syncthreads();
     }
 
-    if (plan.S > 1) {  // slots 2 * item (z) and 2 * item + 1 (u) of 64 floats a thread
+    if (plan.S > 1) {  // slots 2 * item (z) and 2 * item + 1 (u); gated_up_reduce_kernel finishes
       float v[64];
       flatten(ag, v);
-      store_partial(a.part, 2 * item, v);
+      store_partial(a.part, 2 * item, v, R - m0);
       flatten(au, v);
-      store_partial(a.part, 2 * item + 1, v);
-      if (!arrive_last(&a.counters[a.counter_base + tile], plan.S, &s_last)) continue;
-      // slots of split s: 2 (tile S + s) and 2 (tile S + s) + 1
-      float z[64];
-      reduce_partials<false>(a.part, 2 * tile * plan.S, 2, plan.S, z);
-      unflatten(z, ag);
-      reduce_partials<false>(a.part, 2 * tile * plan.S + 1, 2, plan.S, z);
-      unflatten(z, au);
+      store_partial(a.part, 2 * item + 1, v, R - m0);
+      continue;
     }
 
 #pragma unroll
@@ -278,11 +233,10 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   constexpr int kNA = kSplit ? 2 : 1;
   constexpr int kStage = (kNA + 1) * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  __shared__ int s_last;
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
   const int tiles_m = (R + kDM - 1) / kDM;
   const int nk = a.F / kDK;
-  const SplitPlan plan = plan_split(kGather && a.counters != nullptr, tiles_m * tiles_n, nk);
+  const SplitPlan plan = plan_split(kGather && a.split_k, tiles_m * tiles_n, nk);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -378,13 +332,11 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
       __syncthreads();
     }
 
-    if (plan.S > 1) {
+    if (plan.S > 1) {  // slot `item`; down_reduce_kernel finishes
       float v[64];
       flatten(acc, v);
-      store_partial(a.part, item, v);
-      if (!arrive_last(&a.counters[a.counter_base + tile], plan.S, &s_last)) continue;
-      reduce_partials<true>(a.part, tile * plan.S, 1, plan.S, v);
-      unflatten(v, acc);
+      store_partial(a.part, item, v, R - m0);
+      continue;
     }
 
 #pragma unroll
@@ -403,6 +355,65 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   }
 }
 
+// Split epilogues: one work unit per (tile, float4 index q of the flattened
+// accumulators); each thread adds its float4 over the S splits in split order
+// and runs the product's epilogue for those 4 rows of one column.
+constexpr int kReduceWGs = 256;
+
+template <bool kSplit>
+__global__ __launch_bounds__(256) void gated_up_reduce_kernel(DenseArgs a, int tiles_n) {
+  const int R = min(max(*a.n_rows, 0), a.M);
+  const int tiles_m = (R + kDM - 1) / kDM;
+  const SplitPlan plan = plan_split(a.split_k, tiles_m * tiles_n, a.d / kDK);
+  if (plan.S <= 1) return;
+  const int t = threadIdx.x;
+  for (int u = blockIdx.x; u < tiles_m * tiles_n * 16; u += gridDim.x) {
+    const int tile = u >> 4, q = u & 15;
+    const int m0 = (tile % tiles_m) * kDM, n0 = (tile / tiles_m) * kDN;
+    const PartPos pp = part_pos(q, t);
+    if (m0 + pp.row0 >= R) continue;  // never stored
+    const float4 z = sum_partials(a.part, 2 * tile * plan.S, 2, plan.S, q, t);
+    const float4 g = sum_partials(a.part, 2 * tile * plan.S + 1, 2, plan.S, q, t);
+    const float zz[4] = {z.x, z.y, z.z, z.w}, uu[4] = {g.x, g.y, g.z, g.w};
+    const int c = n0 + pp.col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = m0 + pp.row0 + e;
+      if (r < R && c < a.F) {
+        const float h = fmaxf(zz[e], 0.f) * uu[e];
+        const uint32_t hi = f32_to_bf16_rne(h);
+        const size_t o = static_cast<size_t>(r) * a.F + c;
+        a.h_hi[o] = static_cast<uint16_t>(hi);
+        if constexpr (kSplit) a.h_lo[o] = static_cast<uint16_t>(f32_to_bf16_rne(h - __uint_as_float(hi << 16)));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void down_reduce_kernel(DenseArgs a, int tiles_n) {
+  const int R = min(max(*a.n_rows, 0), a.M);
+  const int tiles_m = (R + kDM - 1) / kDM;
+  const SplitPlan plan = plan_split(a.split_k, tiles_m * tiles_n, a.F / kDK);
+  if (plan.S <= 1) return;
+  const int t = threadIdx.x;
+  for (int u = blockIdx.x; u < tiles_m * tiles_n * 16; u += gridDim.x) {
+    const int tile = u >> 4, q = u & 15;
+    const int m0 = (tile % tiles_m) * kDM, n0 = (tile / tiles_m) * kDN;
+    const PartPos pp = part_pos(q, t);
+    if (m0 + pp.row0 >= R) continue;  // never stored
+    const float4 v = sum_partials(a.part, tile * plan.S, 1, plan.S, q, t);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = m0 + pp.row0 + e;
+      if (r < R) {
+        const int dst = a.rows[r];
+        if (dst >= 0 && dst < a.M) a.y[static_cast<size_t>(dst) * a.d + n0 + pp.col] = vv[e];
+      }
+    }
+  }
+}
+
 template <bool kGather, bool kSplit>
 hipError_t launch_pair(const DenseArgs& a, hipStream_t s) {
   const int tiles_nf = (a.F + kDN - 1) / kDN;
@@ -414,12 +425,19 @@ hipError_t launch_pair(const DenseArgs& a, hipStream_t s) {
     g2 = g2 < kPersistentWGs ? g2 : kPersistentWGs;
   }
   DenseArgs up = a, down = a;
-  up.counter_base = 0;
-  down.counter_base = kDenseCounters / 2;
   gated_up_kernel<kGather, kSplit><<<dim3(g1), dim3(256), 0, s>>>(up, tiles_nf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool split = kGather && a.split_k;  // the product kernels may split K
+  if (split) {
+    gated_up_reduce_kernel<kSplit><<<dim3(kReduceWGs), dim3(256), 0, s>>>(up, tiles_nf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   down_kernel<kGather, kSplit><<<dim3(g2), dim3(256), 0, s>>>(down, tiles_nd);
+  e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  down_reduce_kernel<<<dim3(kReduceWGs), dim3(256), 0, s>>>(down, tiles_nd);
   return hipGetLastError();
 }
 

@@ -21,10 +21,10 @@ struct Layout {
   size_t total = 0;
 };
 
-// Header, one flag per row, then the fallback's arrival counters.
+// Header, one flag per row, then the few-row fused kernel's arrival counters.
 size_t ctrl_flags_bytes(int64_t M) { return twell::kCtrlBytes + align256(size_t(M) * 4); }
 size_t ctrl_bytes(int64_t M) { return ctrl_flags_bytes(M) + align256(twell::kDenseCounters * 4); }
-uint32_t* fallback_counters(void* ctrl, int64_t M) {
+uint32_t* row_counters(void* ctrl, int64_t M) {
   return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ctrl) + ctrl_flags_bytes(M));
 }
 
@@ -224,8 +224,7 @@ int sliced_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, cons
 
 int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
                int64_t M, int64_t d, int64_t F, const int32_t* rows, const int32_t* n_rows,
-               uint16_t* h_hi, uint16_t* h_lo, float* y, float* split_part, uint32_t* counters,
-               hipStream_t s) {
+               uint16_t* h_hi, uint16_t* h_lo, float* y, float* split_part, bool split_k, hipStream_t s) {
   if (M == 0) return TWELL_OK;
   twell::DenseArgs a;
   a.x = x;
@@ -241,8 +240,7 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   a.h_lo = h_lo;
   a.y = y;
   a.part = split_part;
-  a.counters = counters;
-  a.counter_base = 0;
+  a.split_k = split_k;
   return hip_status(twell::launch_dense(a, s));
 }
 
@@ -307,7 +305,7 @@ int few_rows_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
   a.spill = spill;
   a.splits = splits_for(M);
   a.part = part;
-  a.counters = fallback_counters(ctrl, M);
+  a.counters = row_counters(ctrl, M);
   return hip_status(twell::launch_fused_updown(a, s));
 }
 
@@ -650,7 +648,7 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
   const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, in->ovf_rows, in->n_ovf, at<uint16_t>(workspace, L.h_hi),
                     at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                    fallback_counters(ctrl, M), static_cast<hipStream_t>(stream));
+                    true, static_cast<hipStream_t>(stream));
 }
 
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
@@ -688,7 +686,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     return TWELL_E_HIP;
   const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                                at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                               fallback_counters(ctrl, M), ss->s);
+                               true, ss->s);
   // join before anything else can be reported, so the caller's stream never
   // runs ahead of work already on the side stream
   const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
@@ -777,7 +775,7 @@ int twell_ffn_forward_gateup(const uint16_t* x, const uint16_t* Wg, const uint16
     return TWELL_E_HIP;
   const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                                at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                               fallback_counters(ctrl, M), ss->s);
+                               true, ss->s);
   const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
   st = hidden_down_impl(Wd, &p, M, d, F, T, C, y, s);
   if (!joined || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return TWELL_E_HIP;
@@ -794,7 +792,7 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
   if (st != TWELL_OK) return st;
   const Layout L = layout(TWELL_OP_DENSE_FFN, M, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, nullptr, nullptr, at<uint16_t>(workspace, L.h_hi),
-                    nullptr, y, nullptr, nullptr, static_cast<hipStream_t>(stream));
+                    nullptr, y, nullptr, false, static_cast<hipStream_t>(stream));
 }
 
 int twell_column_activity(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F,

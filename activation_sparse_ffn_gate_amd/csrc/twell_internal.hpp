@@ -10,7 +10,8 @@ namespace twell {
 // Control block of the gate kernel's overflow set: one 64-bit word whose low
 // half (ctrl[0]) counts rows appended this call and high half (ctrl[1])
 // workgroups finished, then one dedup flag per row, then kDenseCounters
-// arrival counters of the split-K fallback. Zero between calls.
+// arrival counters (the few-row fused kernel's per-row ordered sums). Zero
+// between calls.
 constexpr size_t kCtrlBytes = 256;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -71,10 +72,10 @@ struct DenseArgs {
   uint16_t* h_hi;         // [M, F] bf16 hidden (or its high part)
   uint16_t* h_lo;         // [M, F] low part; nullptr: plain bf16 hidden
   float* y;
-  // Split-K of the gathering kernels (nullptr counters: no split).
+  // Split-K of the gathering kernels: partial tiles, added up by a reduce
+  // launch after each product.
   float* part;            // kDenseSplitSlots partial tiles of 64 KB
-  uint32_t* counters;     // zeroed; gated-up tiles at [0, 128), down tiles at [128, 256)
-  int counter_base;       // set by the launcher for the down kernel
+  bool split_k;           // the gathering kernels may split K
 };
 
 // Partial-tile slots of the split-K fallback: 2 per work item of the gated-up
