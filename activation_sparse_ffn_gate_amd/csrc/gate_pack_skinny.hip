@@ -18,6 +18,15 @@
 // makes every load instruction touch 32 rows, which ran at a fifth of this
 // rate.) The K splits meet through LDS in a fixed order.
 
+// With few tokens even 128-unit workgroups are too few to stream Wg at the
+// HBM rate (64 of them at F = 8192). Given room for partial sums, the gate
+// then runs in two launches: workgroup (tile, q) of the first runs, for the
+// four unit groups, exactly the k-steps that wave (unit group, K split q) of
+// the single launch runs (a quarter of every chunk) and stores the four
+// accumulators; the second is the single-launch kernel with each wave taking
+// its accumulator from split q instead of a K loop, then adding the splits in
+// the same order. So z, and every packed bit, is the same in both forms.
+//
 // Packing: per accumulator register a 64-bit ballot of z > 0 gives two tokens'
 // activity over the wave's 32 units; the waves of a tile exchange per-token
 // counts through LDS, so a unit's slot is the count in lower waves plus its
@@ -59,7 +68,10 @@ __device__ __forceinline__ uint32_t sk_off(int r, int p) {
   return static_cast<uint32_t>(r * kRowB + ((p ^ (r & 15)) << 4));
 }
 
-template <int kT, bool kDebug, bool kAct, int RB>
+// K chunks (256 values) a split workgroup preloads: d <= 2048 splits.
+constexpr int kMaxSplitChunks = 8;
+
+template <int kT, bool kDebug, bool kAct, int RB, bool kFromParts = false>
 __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateArgs a, int tiles_m) {
   using S = SkinnyShape<RB>;
   constexpr int kSM = S::kSM;
@@ -78,6 +90,36 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   const int n0 = (blockIdx.x / tiles_m) * kSN;
   const int r = lane & 31, half = lane >> 5;
 
+  f32x16_t acc[RB];
+  if constexpr (kFromParts) {
+    // Launched with 4 waves (kh = 0): unit group wn's sums of the K splits,
+    // added in split order as the single launch adds its waves' sums (float4s
+    // of rows past M were not stored: they read as zero, those rows never count).
+    const float4* src = reinterpret_cast<const float4*>(a.kpart) +
+                        (static_cast<size_t>(blockIdx.x) * kKS * 4 + wn) * 64 * 4 * RB + lane * 4 * RB;
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bool live = m0 + 32 * b + 8 * g + 4 * half < a.M;
+        float4 v[kKS];
+#pragma unroll
+        for (int q = 0; q < kKS; ++q)
+          v[q] = live ? src[static_cast<size_t>(q) * 4 * 64 * 4 * RB + 4 * b + g] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 t = v[0];
+#pragma unroll
+        for (int q = 1; q < kKS; ++q) {
+          t.x += v[q].x;
+          t.y += v[q].y;
+          t.z += v[q].z;
+          t.w += v[q].w;
+        }
+        acc[b][4 * g] = t.x;
+        acc[b][4 * g + 1] = t.y;
+        acc[b][4 * g + 2] = t.z;
+        acc[b][4 * g + 3] = t.w;
+      }
+  } else {
   // Loads: every wave instruction reads 1 KB contiguous (whole rows' K chunk).
   // Thread tid holds pieces q = tid + 1024 i of the chunk's kRows x kPieces:
   // rows below 128 are Wg rows, the rest x rows. Rows past M or F read a valid
@@ -115,7 +157,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   // kKc / 16 k-steps; step s uses piece 2s + half of its rows (A: token rows,
   // one accumulator block per 32 tokens; B: unit rows).
   constexpr int kStepsPerWave = S::kKc / 16 / kKS;
-  f32x16_t acc[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -162,6 +203,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
       mma((ck + 2) & 1);
     }
   }
+  }
   __syncthreads();  // every wave is done with the stages
 
   // K splits: splits 1 .. kKS-1 hand their sums to split 0, which adds them in
@@ -182,12 +224,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   int appended = 0;
 
   if (kh == 0) {
+    if constexpr (!kFromParts) {
 #pragma unroll
-    for (int j = 0; j < kKS - 1; ++j)
+      for (int j = 0; j < kKS - 1; ++j)
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
+        for (int b = 0; b < RB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[b][v] += s_red[j][wn][lane][16 * b + v];
+          for (int v = 0; v < 16; ++v) acc[b][v] += s_red[j][wn][lane][16 * b + v];
+    }
     const int ucol = n0 + wn * 32 + r;  // this lane's unit
     const bool unit_ok = ucol < a.F;
 #pragma unroll
@@ -270,12 +314,119 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   overflow_finalize(a, appended, s_last);
 }
 
+// First launch of the K split (RB = 1 only): workgroup (tile, q), 4 waves,
+// wave wn = unit group wn. Each chunk's quarter q (pieces 8q .. 8q + 7 of its
+// 32) is staged in LDS as 128-byte rows, 16-byte pieces XOR-swizzled by
+// (row / 2) mod 8 so the 16 rows a ds_read_b128 serves at once fall in 16
+// bank groups; the MFMAs are those of wave (wn, kh = q) of the single launch,
+// chunk by chunk in the same order.
+__global__ __launch_bounds__(256) void gate_skinny_split_kernel(GateArgs a, int tiles_m) {
+  using S = SkinnyShape<1>;
+  constexpr int kQP = S::kPieces / kKS;  // pieces of a chunk per split: 8
+  constexpr int kRowQ = kQP * 16;
+  constexpr int kStageQ = S::kRows * kRowQ;
+  constexpr int kLoadsQ = S::kRows * kQP / 256;  // 16-byte loads per thread per chunk
+  static_assert(S::kRows * kQP % 256 == 0 && kQP == 8, "whole loads per thread");
+  constexpr int kStepsPerWave = S::kKc / 16 / kKS;
+  static_assert(2 * kStepsPerWave == kQP, "a wave's k-steps cover its quarter");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = blockIdx.x % kKS;
+  const int tile = blockIdx.x / kKS;
+  const int m0 = (tile % tiles_m) * S::kSM;
+  const int n0 = (tile / tiles_m) * kSN;
+  const int r = lane & 31, half = lane >> 5;
+  auto soff_of = [](int row, int pq) { return static_cast<uint32_t>(row * kRowQ + ((pq ^ ((row >> 1) & 7)) << 4)); };
+
+  // rows below 128 are Wg rows, the rest x rows; rows past M or F read a valid row
+  const uint32_t row_bytes = static_cast<uint32_t>(a.d) * 2u;
+  const char* xb = reinterpret_cast<const char*>(a.x);
+  const char* wb = reinterpret_cast<const char*>(a.Wg);
+  uint32_t goff[kLoadsQ], soff[kLoadsQ];
+  bool isw[kLoadsQ];
+#pragma unroll
+  for (int i = 0; i < kLoadsQ; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / kQP, pq = idx % kQP;
+    isw[i] = row < kSN;
+    const int grow = isw[i] ? min(n0 + row, a.F - 1) : min(m0 + row - kSN, a.M - 1);
+    goff[i] = static_cast<uint32_t>(grow) * row_bytes + static_cast<uint32_t>(q * kQP + pq) * 16u;
+    soff[i] = soff_of(row, pq);
+  }
+  struct Regs {
+    u32x4_t v[kLoadsQ];
+  };
+  auto gload = [&](Regs& g, int ck) {
+    const uint32_t k = static_cast<uint32_t>(ck) * S::kRowB;
+#pragma unroll
+    for (int i = 0; i < kLoadsQ; ++i)
+      g.v[i] = *reinterpret_cast<const u32x4_t*>((isw[i] ? wb : xb) + goff[i] + k);
+  };
+  auto sstore = [&](const Regs& g, int st) {
+#pragma unroll
+    for (int i = 0; i < kLoadsQ; ++i) lds_store16(smem + st * kStageQ, soff[i], g.v[i]);
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  auto mma = [&](int st) {
+    const uint8_t* base = smem + st * kStageQ;
+#pragma unroll
+    for (int j = 0; j < kStepsPerWave; ++j) {
+      const int pq = 2 * j + half;  // piece 2 (q kStepsPerWave + j) + half of the chunk
+      const u32x4_t bf = lds_load16(base, soff_of(wn * 32 + r, pq));
+      const u32x4_t af = lds_load16(base, soff_of(kSN + r, pq));
+      acc = mfma_32x32x16(af, bf, acc);
+    }
+  };
+  // Every chunk's loads go out at once (at most kMaxSplitChunks chunks: 40
+  // sixteen-byte loads a thread), so the workgroup waits for one memory round
+  // trip rather than one every few chunks; chunks then pass through two LDS
+  // stages in order.
+  const int nck = a.d / S::kKc;
+  Regs g[kMaxSplitChunks];
+  static_for<0, kMaxSplitChunks>([&](auto I) { gload(g[I.value], min(I.value, nck - 1)); });
+  static_for<0, kMaxSplitChunks>([&](auto I) {
+    constexpr int ck = I.value;
+    if (ck < nck) {  // uniform
+      sstore(g[ck], ck & 1);
+      __syncthreads();
+      mma(ck & 1);
+    }
+  });
+  // the accumulator, float4 g holding rows 8 g + 4 half .. +3 of the tile
+  float4* dst = reinterpret_cast<float4*>(a.kpart) + ((static_cast<size_t>(tile) * kKS + q) * 4 + wn) * 64 * 4 + lane * 4;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    if (m0 + 8 * g + 4 * half < a.M) dst[g] = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+}
+
 template <int RB>
 hipError_t launch_rb(const GateArgs& a, hipStream_t s) {
   const int tiles_m = (a.M + 32 * RB - 1) / (32 * RB);
   const int tiles_n = (a.F + kSN - 1) / kSN;
   const dim3 grid(tiles_m * tiles_n), block(64 * kWaves);
   const bool dbg = a.z_debug != nullptr, act = a.col_active != nullptr;
+  if (RB == 1 && a.kpart != nullptr && a.kpart_bytes >= skinny_kpart_bytes(a.M, a.d, a.F) &&
+      skinny_kpart_bytes(a.M, a.d, a.F) > 0) {
+    gate_skinny_split_kernel<<<dim3(tiles_m * tiles_n * kKS), dim3(256), 0, s>>>(a, tiles_m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 block4(256);  // the unit groups' first waves only (kh = 0)
+    if (a.T == 128) {
+      if (dbg) gate_pack_skinny_kernel<128, true, false, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+      else if (act) gate_pack_skinny_kernel<128, false, true, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+      else gate_pack_skinny_kernel<128, false, false, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+    } else {
+      if (dbg) gate_pack_skinny_kernel<64, true, false, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+      else if (act) gate_pack_skinny_kernel<64, false, true, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+      else gate_pack_skinny_kernel<64, false, false, RB, true><<<grid, block4, 0, s>>>(a, tiles_m);
+    }
+    return hipGetLastError();
+  }
   if (a.T == 128) {
     if (dbg) gate_pack_skinny_kernel<128, true, false, RB><<<grid, block, 0, s>>>(a, tiles_m);
     else if (act) gate_pack_skinny_kernel<128, false, true, RB><<<grid, block, 0, s>>>(a, tiles_m);
@@ -289,6 +440,13 @@ hipError_t launch_rb(const GateArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+size_t skinny_kpart_bytes(int64_t M, int64_t d, int64_t F) {
+  if (M <= 0 || M > kSkinnyRb1MaxM || d > kMaxSplitChunks * SkinnyShape<1>::kKc) return 0;
+  const int64_t tiles = ((M + 31) / 32) * ((F + kSN - 1) / kSN);
+  if (tiles >= 128) return 0;  // enough workgroups already (measured: splitting 128 was slower)
+  return size_t(tiles) * kKS * 4 * 64 * 16 * sizeof(float);
+}
 
 hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s) {
   // 32-token tiles while they already give a few hundred workgroups' worth of

@@ -150,7 +150,8 @@ twell_packed packed_in_ws(void* ws, const Layout& L) {
 
 int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, int64_t F, int32_t T,
                    int32_t C, const twell_packed* out, float* z_debug, uint32_t* ctrl,
-                   hipStream_t s, uint32_t* col_active = nullptr, float* spill = nullptr) {
+                   hipStream_t s, uint32_t* col_active = nullptr, float* spill = nullptr,
+                   float* kpart = nullptr, size_t kpart_bytes = 0) {
   if (M == 0) return hip_status(twell::launch_set_i32(out->n_ovf, 0, s));
   twell::GateArgs a;
   a.x = x;
@@ -169,6 +170,8 @@ int gate_pack_impl(const uint16_t* x, const uint16_t* Wg, int64_t M, int64_t d, 
   a.z_debug = z_debug;
   a.col_active = col_active;
   a.spill = spill;
+  a.kpart = kpart;
+  a.kpart_bytes = kpart_bytes;
   return hip_status(twell::launch_gate_pack(a, s));
 }
 
@@ -298,8 +301,11 @@ int splits_for(int64_t M) { return int(std::min<int64_t>(16, std::max<int64_t>(1
 
 int few_rows_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd, int64_t M,
                      int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl, const twell_packed& p,
-                     float* spill, float* part, hipStream_t s) {
-  int st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill);
+                     float* spill, float* part, size_t part_bytes, hipStream_t s) {
+  // The gate's K-split partial sums (if it splits) are consumed before the
+  // fused kernel writes its partial rows to the same region.
+  int st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill,
+                          part, part_bytes);
   if (st != TWELL_OK) return st;
   twell::FusedArgs a = fused_args(x, WuT, Wd, &p, M, d, F, T, C, y);
   a.spill = spill;
@@ -339,7 +345,8 @@ StaticLayout static_layout(int64_t M, int64_t d, int64_t F, int32_t T, int32_t C
   L.ovf_rows = take(m * 4);
   L.n_ovf = take(4);
   L.spill = take(m * size_t(F) * 4);
-  L.part = take(size_t(splits_for(std::max<int64_t>(M, 1))) * m * size_t(d) * 4);
+  L.part = take(std::max(size_t(splits_for(std::max<int64_t>(M, 1))) * m * size_t(d) * 4,
+                         twell::skinny_kpart_bytes(M, d, F)));
   L.total = off;
   return L;
 }
@@ -671,7 +678,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     // the partial rows (at most 512 rows of d floats) its split-K region; both
     // are idle on this path.
     return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, p, at<float>(workspace, L.h_hi),
-                            at<float>(workspace, L.split), s);
+                            at<float>(workspace, L.split), twell::kDenseSplitBytes, s);
   }
   int dev = -1;
   if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
@@ -720,7 +727,8 @@ int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16
   p.ovf_rows = reinterpret_cast<int32_t*>(base + L.ovf_rows);
   p.n_ovf = reinterpret_cast<int32_t*>(base + L.n_ovf);
   return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, base + L.ctrl, p,
-                          reinterpret_cast<float*>(base + L.spill), reinterpret_cast<float*>(base + L.part), s);
+                          reinterpret_cast<float*>(base + L.spill), reinterpret_cast<float*>(base + L.part),
+                          L.total - L.part, s);
 }
 
 int twell_gateup_pack(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, int64_t M, int64_t d,

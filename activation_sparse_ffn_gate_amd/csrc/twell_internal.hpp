@@ -41,6 +41,10 @@ struct GateArgs {
   int32_t* rec_slot = nullptr;
   int32_t* rec_n = nullptr;
   int rec_cap = 0;
+  // Small-batch kernel: room for the K split across workgroups (nullable:
+  // single launch); kpart_bytes must cover skinny_kpart_bytes(M, d, F).
+  float* kpart = nullptr;
+  size_t kpart_bytes = 0;
 };
 
 struct FusedArgs {
@@ -111,6 +115,9 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
 constexpr int kSkinnyMaxM = 256;
 constexpr int kSkinnyRb1MaxM = 128;  // up to here 32-token tiles, then 64-token tiles
 hipError_t launch_gate_pack_skinny(const GateArgs& a, hipStream_t s);
+// Bytes of K-split partial sums the small-batch gate uses for M rows when it
+// splits K across workgroups (0: it does not split at this shape).
+size_t skinny_kpart_bytes(int64_t M, int64_t d, int64_t F);
 hipError_t launch_sliced_updown(const SlicedArgs& a, hipStream_t s);
 // d and F the sliced kernels take (lane splits exist, weights below 2 GiB).
 bool sliced_supports(int64_t d, int64_t F);

@@ -184,8 +184,9 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
  * held from the library's first use on that GPU until the process ends. It
  * holds a control block sized for 256 rows, the packing (M (F/T) C 5 +
  * M (F/T) 2 + 4 M bytes), the z of overflowing tiles (M F 4 bytes) and the
- * partial rows of long rows (min(16, 512 / M) M d 4 bytes), each rounded up
- * to 256 bytes. Every call on one GPU uses the same buffer: calls that may
+ * partial rows of long rows (min(16, 512 / M) M d 4 bytes) or, where larger,
+ * the gate's K-split partial sums (up to 128 rows, while fewer than 256 tiles
+ * of 32 rows x 128 units: 64 KB a tile), each rounded up to 256 bytes. Every call on one GPU uses the same buffer: calls that may
  * overlap on a GPU (several streams or threads) race, and the caller must
  * order them. Returns TWELL_E_UNSUPPORTED for M > 256, TWELL_E_SCRATCH when
  * the shape needs more than the buffer, TWELL_E_HIP when the buffer's device
