@@ -22,6 +22,7 @@ from _parity import (
     check_y,
     host_packing,
     to_device,
+    used_slots,
     y_errors,
 )
 
@@ -143,6 +144,11 @@ def test_components_compose(name):
     p = tw.gate_pack(x, Wg, w.T, w.C)
     g = host_packing(p)
     assert np.array_equal(view["counts"], g["counts"]) and np.array_equal(view["ovf"], g["ovf"])
+    # the forward's gate (for few tokens split over K across workgroups, in the
+    # same sum order) packs the same bits as the standalone single launch
+    used = used_slots(g["counts"], w.C)
+    assert np.array_equal(view["idx"][used], g["idx"][used])
+    assert np.array_equal(view["vals"][used].view(np.uint32), g["vals"][used].view(np.uint32))
     # the forward's choice: the sliced form above 256 rows, where d allows it
     updown = tw.sliced_updown if (w.M > 256 and sliced_ok(w.d)) else tw.fused_updown
     y = updown(x, WuT, Wd, p, y=nan_y(w.M, w.d))
