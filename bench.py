@@ -67,7 +67,8 @@ def _counter_kib(path, counter, kernel=None):
 def record_traffic(root, workload):
     """Write profiles/traffic.json from rocprofv3 --pmc runs stored under root:
     pmc_<workload>_<leg>_fetch / _write for leg in gate, fused and sliced (the
-    sliced leg holds both of its kernels; their traffic is summed), scaled by
+    sliced leg holds its three kernels, row lists, up and down; their traffic
+    is summed), scaled by
     pmc_copy_fetch / pmc_copy_write of a plain copy of known size. Workloads
     already recorded from the same kernel sources are kept."""
     cf = COPY_BYTES / 1024.0 / _counter_kib(os.path.join(root, "pmc_copy_fetch"), "FETCH_SIZE")
@@ -81,7 +82,7 @@ def record_traffic(root, workload):
             rec["workloads"] = old.get("workloads", {})
     ent = {}
     for leg, name, kernels in (("gate", "gate_pack", ["gate_pack"]), ("fused", "fused_updown", ["fused_updown"]),
-                               ("sliced", "sliced_updown", ["sliced_up_kernel", "sliced_down_kernel"])):
+                               ("sliced", "sliced_updown", ["row_list_kernel", "sliced_up_kernel", "sliced_down_kernel"])):
         d_f = os.path.join(root, f"pmc_{workload}_{leg}_fetch")
         if not os.path.isdir(d_f):
             continue
