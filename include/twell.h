@@ -42,7 +42,9 @@
  *    before its first use; every call leaves it zero-filled again when it
  *    completes (stream order), so one buffer sized for the largest M serves
  *    every later call. It holds the overflow-set counters, one deduplication
- *    flag per row and the arrival counters of the fallback's split products.
+ *    flag per row and the arrival counters of the few-row forward's split
+ *    rows (twell_dense_fallback checks it but no longer writes it: its split
+ *    products are added by reduce launches).
  *    Calls sharing a control block must not run concurrently.
  *  - With M == 0 nothing is computed; x and y may then be NULL.
  */
@@ -120,12 +122,15 @@ int twell_fused_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* W
  * of WuT and Wd, F * d / 8 bf16 per matrix, which stays in that XCD's L2
  * (which rows are gathered and what is summed are as in the pages' inference
  * kernel: tgviewer.app Telegram post, part "Инференс"; aimodeling.com summary,
- * paragraph 3). Two launches: the first stores, per stored unit and slice,
- * g_j * (x_r . WuT[j]) over that slice's columns; the second sums the 8
+ * paragraph 3). Three launches: the first turns each row's TwELL tiles into
+ * one contiguous list of (unit, gate value) entries in (tile, slot) order and
+ * its length (-1 for an overflow row); the second stores, per listed unit and
+ * slice, g_j * (x_r . WuT[j]) over that slice's columns; the third sums the 8
  * partials of each unit in slice order and accumulates h_j * Wd[j] over its
  * slice. Same contract for y as twell_fused_updown (overflow rows untouched).
  * workspace: >= twell_workspace_bytes(TWELL_OP_SLICED_UPDOWN, ...)
- * = 8 * M * (F / T) * C fp32 partials.
+ * = 8 M (F / T) C fp32 partials, M (F / T) C 8-byte list entries and M
+ * lengths, each rounded up to 256 bytes.
  * d must be one of 256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072,
  * 3584, 4096, 5120, 6144, 7168, 8192 (d / 64 = 2^a * b with b in {1, 3, 5, 7})
  * and F * d * 2 < 2^31 (each weight matrix below 2 GiB), otherwise
@@ -141,7 +146,8 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
  * MFMA products, fp32 accumulation and the hidden vector carried as a bf16
  * hi/lo pair. n_ovf is read on the device (no host synchronisation); other rows
  * of y are untouched. When the list is short the K loops are split over more
- * workgroups and their partial tiles added in a fixed order (deterministic).
+ * workgroups, and a reduce launch after each product adds their partial
+ * tiles in a fixed order (deterministic).
  * ctrl: >= twell_ctrl_bytes(M) (see above);
  * workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FALLBACK, ...). */
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
@@ -168,7 +174,11 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
  * concurrent callers on that GPU.
  * Up to 256 rows: the gate also keeps every z of each (row, tile) whose count
  * exceeds C in the workspace, and the fused kernel does overflow rows from it
- * (their whole active set, still only gathers): two launches, no fallback.
+ * (their whole active set, still only gathers): two launches, no fallback;
+ * for a few tokens (fewer than 128 gate tiles of 32 tokens x 128 units,
+ * d <= 2048) the gate splits its K over workgroups in a first launch, with
+ * the same sums in the same order, so the packing is bit-identical to
+ * twell_gate_pack's.
  * ctrl: >= twell_ctrl_bytes(M); workspace: >= twell_workspace_bytes(TWELL_OP_FFN_FORWARD, ...). */
 int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                       const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
