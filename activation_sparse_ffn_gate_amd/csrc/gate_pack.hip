@@ -14,18 +14,16 @@
 // ahead so HBM/MALL latency hides behind the MFMAs. Small batches use
 // gate_pack_skinny.hip instead (see launch_gate_pack).
 //
-// Packing. The forward's instance stages the finished tile through the idle
-// LDS ring, 128 token rows at a time: the two waves that own those rows write
-// their accumulators, then every thread takes one (token, 128 units) segment
-// and builds its activity mask with plain compares (unit c at bit c), so the
+// Packing. The finished tile is staged through the idle LDS ring, 128 token
+// rows at a time: the two waves that own those rows write their
+// accumulators, then every thread takes one (token, 128 units) segment and
+// builds its activity mask with plain compares (unit c at bit c), so the
 // per-tile count is a popcount and the stored slots are the first C set bits
 // in ascending unit order, each found with a count-trailing-zeros. Only slots
 // < C are stored (fp32 value, tile-local index); the count is stored
-// unclamped. The debug, column-activity and spill instances pack straight from
-// the accumulators instead: in the MFMA layout one register holds, across the
-// 64 lanes, 32 consecutive units of two tokens, so a 64-bit ballot of (z > 0)
-// gives both tokens' masks and a lane's slot is the popcount of the mask bits
-// below it. Both forms produce the same bits; the tests compare them.
+// unclamped. The training instance also copies all T z of each overflowing
+// (token, tile) into a spill record. The column-activity instance packs
+// nothing: per 32-unit block it ORs the ballots of z > 0 over its tokens.
 //
 // Overflow rows (some tile count > C) are appended to a deduplicated list with
 // device-scope atomics. The last workgroup to finish publishes the list length
@@ -245,7 +243,26 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
       }
   }
 
-  if constexpr (!kAct && !kSpill) {
+  if constexpr (kAct) {
+    // Column activity only (its packing would be thrown away): per 32-unit
+    // block the OR over the wave's tokens of the ballots of z > 0, one atomic
+    // OR per block. No packing, so no overflow set and no finalize.
+    uint64_t act[4] = {0, 0, 0, 0};
+    static_for<0, 64>([&](auto g) {
+      constexpr int mb = decltype(g)::value / 16, v = decltype(g)::value % 16;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) act[nb] |= __ballot(acc[mb][nb][v] > 0.f);
+    });
+    // both halves of a ballot hold the same 32 units, for two tokens; blocks
+    // past the last tile are skipped
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t word = static_cast<uint32_t>(act[nb]) | static_cast<uint32_t>(act[nb] >> 32);
+      if (tile0 + nb / kBlocksPerTile < nT && word != 0u && lane == 0)
+        atomicOr(&a.col_active[(wcol0 >> 5) + nb], word);
+    }
+    return;
+  } else {
     // Packing through LDS. The ring is idle after the K loop; each of two
     // passes holds the 128 token rows of one half of the tile (row-major, rows
     // padded by 4 floats so the column reads below fall in distinct banks).
@@ -302,10 +319,35 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
 #pragma unroll
       for (int k = 0; k < kTilesPerThread; ++k) {
         const int tile = (n0 + th * 128) / kT + k;
-        if (token < a.M && tile < nT) {
-          int cnt = 0;
+        const bool valid = token < a.M && tile < nT;
+        int cnt = 0;
 #pragma unroll
-          for (int w = 0; w < kWordsPerTile; ++w) cnt += __popc(m[k * kWordsPerTile + w]);
+        for (int w = 0; w < kWordsPerTile; ++w) cnt += __popc(m[k * kWordsPerTile + w]);
+        if constexpr (kSpill) {
+          // Every z of an overflowing (token, tile) goes to a spill record. The
+          // wave takes its records with one atomic; lanes number theirs by
+          // rank. The slot map names the record even past the list's
+          // capacity, so readers see that it was not stored.
+          const bool ov = valid && cnt > C;
+          const uint64_t bal = __ballot(ov);
+          if (bal != 0u) {  // wave-uniform
+            const int first = __builtin_ctzll(bal);
+            int rec0 = 0;
+            if (lane == first) rec0 = atomicAdd(reinterpret_cast<int*>(a.ctrl + 2), __popcll(bal));
+            rec0 = __builtin_amdgcn_readlane(rec0, first);
+            if (ov) {
+              const int rec = rec0 + static_cast<int>(mask_rank(bal));
+              a.rec_slot[static_cast<size_t>(token) * nT + tile] = rec;
+              if (rec < a.rec_cap) {
+                float4* rz = reinterpret_cast<float4*>(a.rec_z + static_cast<size_t>(rec) * kT);
+                const float4* src = reinterpret_cast<const float4*>(zr + k * kT);
+#pragma unroll
+                for (int q = 0; q < kT / 4; ++q) rz[q] = src[q];
+              }
+            }
+          }
+        }
+        if (valid) {
           a.counts[static_cast<size_t>(token) * nT + tile] = static_cast<uint16_t>(cnt);
           if (cnt > C) appended |= overflow_append(a, token);
           const uint32_t base = static_cast<uint32_t>(token) * row_slots + static_cast<uint32_t>(tile * C);
@@ -327,123 +369,14 @@ __global__ __launch_bounds__(256, 1) void gate_pack_kernel(GateArgs a, int tiles
       waitcnt<63, 0>();
       raw_barrier();  // every thread is done reading before the next pass writes
     }
+    // Only overflow-list appends take the release fence: nothing in this
+    // kernel reads the spill records (the launch boundary publishes them),
+    // and the record counter is an atomic whose returned value every wave
+    // has used before the workgroup arrives, so the last arrival reads it
+    // whole. (Fencing every spilling wave cost 40% of the layer's gate time
+    // on the heavy-tailed layer: each fence writes back the XCD's L2.)
     overflow_finalize(a, appended, reinterpret_cast<int*>(smem));
-    return;
   }
-
-  // cnt[tt][h] of lane L = count of token wrow0 + 64 h + L in TwELL tile tile0 + tt
-  int cnt[kTilesPerWave][2];
-#pragma unroll
-  for (int tt = 0; tt < kTilesPerWave; ++tt) cnt[tt][0] = cnt[tt][1] = 0;
-
-  uint64_t act[4] = {0, 0, 0, 0};  // column activity (kAct): OR of the ballots
-  int spilled = 0;                 // kSpill: this thread wrote spill records
-
-  static_for<0, 64>([&](auto g) {
-    constexpr int mb = decltype(g)::value / 16, v = decltype(g)::value % 16;
-    uint64_t bal[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) bal[nb] = __ballot(acc[mb][nb][v] > 0.f);
-    if constexpr (kAct) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) act[nb] |= bal[nb];
-    }
-    if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;  // both tokens inactive here
-    constexpr int rl_lo = mb * 32 + acc_row(v, 0);  // token of lanes 0-31; lanes 32-63: +4
-    constexpr int h = rl_lo >> 6, l_lo = rl_lo & 63;
-    const uint32_t row = static_cast<uint32_t>(wrow0 + rl_lo + 4 * half);
-#pragma unroll
-    for (int tt = 0; tt < kTilesPerWave; ++tt) {
-      const int tile = tile0 + tt;
-      if (tile >= nT) continue;  // T = 64 and this half of the wave lies past F
-      uint32_t p_lo[kBlocksPerTile + 1], p_hi[kBlocksPerTile + 1];  // running prefixes
-      p_lo[0] = p_hi[0] = 0;
-#pragma unroll
-      for (int q = 0; q < kBlocksPerTile; ++q) {
-        const uint64_t bq = bal[tt * kBlocksPerTile + q];
-        p_lo[q + 1] = p_lo[q] + __popc(static_cast<uint32_t>(bq));
-        p_hi[q + 1] = p_hi[q] + __popc(static_cast<uint32_t>(bq >> 32));
-      }
-      cnt[tt][h] = writelane<l_lo>(cnt[tt][h], static_cast<int>(p_lo[kBlocksPerTile]));
-      cnt[tt][h] = writelane<l_lo + 4>(cnt[tt][h], static_cast<int>(p_hi[kBlocksPerTile]));
-      // Whether every active unit of both tokens fits in the C slots.
-      const bool fits = p_lo[kBlocksPerTile] <= static_cast<uint32_t>(C) &&
-                        p_hi[kBlocksPerTile] <= static_cast<uint32_t>(C);
-      if constexpr (kSpill) {
-        // Every z of an overflowing (token, tile) goes to a spill record: lane
-        // 0 (token of lanes 0-31) and lane 32 take the records with a vector
-        // atomic, then each half writes its token's T values.
-        if (!fits) {
-          const bool ov_lo = p_lo[kBlocksPerTile] > static_cast<uint32_t>(C);
-          const bool ov_hi = p_hi[kBlocksPerTile] > static_cast<uint32_t>(C);
-          int rec = 0;
-          if ((lane == 0 && ov_lo) || (lane == 32 && ov_hi)) rec = atomicAdd(reinterpret_cast<int*>(a.ctrl + 2), 1);
-          const int rec_me = half ? __builtin_amdgcn_readlane(rec, 32) : __builtin_amdgcn_readlane(rec, 0);
-          if (half ? ov_hi : ov_lo) {
-            // the slot map names the record even past the list's capacity, so
-            // readers see that it was not stored
-            if (col == 0) a.rec_slot[static_cast<size_t>(row) * nT + tile] = rec_me;
-            if (rec_me < a.rec_cap) {
-              float* rz = a.rec_z + static_cast<size_t>(rec_me) * kT;
-#pragma unroll
-              for (int q = 0; q < kBlocksPerTile; ++q) rz[q * 32 + col] = acc[mb][tt * kBlocksPerTile + q][v];
-            }
-          }
-          spilled = 1;
-        }
-      }
-      const uint32_t base = row * row_slots + static_cast<uint32_t>(tile * C);
-#pragma unroll
-      for (int q = 0; q < kBlocksPerTile; ++q) {
-        const int nb = tt * kBlocksPerTile + q;
-        const uint64_t bq = bal[nb];
-        if (bq == 0) continue;  // no active unit in these 32 columns
-        // slot = active units left of this one in the token's tile:
-        // earlier blocks (p_lo / p_hi) plus lower lanes of this block.
-        const uint32_t pre_hi = p_hi[q] - __popc(static_cast<uint32_t>(bq));
-        const uint32_t slot = mask_rank(bq) + (half ? pre_hi : p_lo[q]);
-        const float z = acc[mb][nb][v];
-        if (z > 0.f && (fits || slot < static_cast<uint32_t>(C))) {
-          store_at(a.vals, (base + slot) * 4u, z);
-          store_at(a.idx, base + slot, static_cast<uint8_t>(q * 32 + col));
-        }
-      }
-    }
-  });
-
-  // Column activity: one OR per 32-unit block (both halves of a ballot hold
-  // the same 32 units, for two tokens), skipped past the last tile.
-  if constexpr (kAct) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const uint32_t word = static_cast<uint32_t>(act[nb]) | static_cast<uint32_t>(act[nb] >> 32);
-      if (tile0 + nb / kBlocksPerTile < nT && word != 0u && lane == 0)
-        atomicOr(&a.col_active[(wcol0 >> 5) + nb], word);
-    }
-  }
-
-  // Counts: lane L writes tokens wrow0 + L and wrow0 + 64 + L; overflow rows
-  // join the set.
-  int appended = 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = wrow0 + 64 * h + lane;
-    if (row < a.M) {
-      bool over = false;
-#pragma unroll
-      for (int tt = 0; tt < kTilesPerWave; ++tt) {
-        if (tile0 + tt < nT) {
-          a.counts[static_cast<size_t>(row) * nT + tile0 + tt] = static_cast<uint16_t>(cnt[tt][h]);
-          over |= cnt[tt][h] > C;
-        }
-      }
-      if (over) appended |= overflow_append(a, row);
-    }
-  }
-
-  // The last workgroup publishes n_ovf and clears the control block; the
-  // stage buffers are idle now and hold its flag.
-  overflow_finalize(a, appended | spilled, reinterpret_cast<int*>(smem));
 }
 
 __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }

@@ -101,9 +101,8 @@ def test_packing_bitexact(name):
     assert np.abs(z - Z).max() <= 1e-4 * rms.max()
     ref = O.pack_twell(z, w.T, w.C)
     check_packing_bitexact(host_packing(p), ref)
-    # the instance without z output (the forward's; above 256 rows it packs
-    # through LDS instead of from the accumulators) computes the same z, so its
-    # packing equals the same reference bit for bit
+    # the instance without z output (the forward's) computes the same z, so
+    # its packing equals the same reference bit for bit
     p_fwd, _ = run_gate(inp, debug=False)
     check_packing_bitexact(host_packing(p_fwd), ref)
 
