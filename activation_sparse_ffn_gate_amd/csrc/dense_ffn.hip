@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
 // Split epilogues: one work unit per (tile, float4 index q of the flattened
 // accumulators); each thread adds its float4 over the S splits in split order
 // and runs the product's epilogue for those 4 rows of one column.
-constexpr int kReduceWGs = 256;
+constexpr int kReduceWGs = 2048;  // at most 127 split tiles x 16 units: one unit a workgroup
 
 template <bool kSplit>
 __global__ __launch_bounds__(256) void gated_up_reduce_kernel(DenseArgs a, int tiles_n) {
