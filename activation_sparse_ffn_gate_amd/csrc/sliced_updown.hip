@@ -350,12 +350,14 @@ __global__ __launch_bounds__(64) void sliced_down_kernel(SlicedArgs a) {
     }
   });
 
+  // y is stored non-temporal: an XCD's slice of it (4 MB at M = 4096,
+  // d = 2048, as large as its L2) would otherwise evict its Wd slice.
   float* yr = a.y + static_cast<size_t>(row) * a.d + col0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     if (v % G == grp && (G > 1 || lane < L)) {
-      *reinterpret_cast<float4*>(yr + v * 8 * L) = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
-      *reinterpret_cast<float4*>(yr + v * 8 * L + 4) = make_float4(acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
+      store16_nt(yr + v * 8 * L, acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+      store16_nt(yr + v * 8 * L + 4, acc[v][4], acc[v][5], acc[v][6], acc[v][7]);
     }
   }
 }

@@ -21,6 +21,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -165,6 +166,13 @@ __device__ __forceinline__ u32x4_t lds_frag(const uint8_t* tile, int row0, int k
 
 __device__ __forceinline__ u32x4_t gload16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// 16-byte store with the non-temporal hint, for output written once and not
+// read again by the launch: it keeps L2 for the data the launch reuses.
+__device__ __forceinline__ void store16_nt(float* p, float a, float b, float c, float d) {
+  const f32x4_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
 }
 
 // ------------------------------------------------------------------ LDS DMA
