@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     ffn_backward,
     ffn_forward,
     ffn_forward_static,
+    ffn_forward_timed,
     ffn_forward_gateup,
     fused_updown,
     gate_pack,

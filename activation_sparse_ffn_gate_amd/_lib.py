@@ -68,6 +68,8 @@ _SIGNATURES = {
     "twell_sliced_updown": (ctypes.c_int, [_P, _P, _P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P]),
     "twell_dense_fallback": (ctypes.c_int, [_P, _P, _P, _P, _PK, _I64, _I64, _I64, _P, _P, _SZ, _P, _SZ, _P]),
     "twell_ffn_forward": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
+    "twell_ffn_forward_timed": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P, _SZ,
+                                               _P, _P, _P]),
     "twell_ffn_forward_static": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P]),
     "twell_gateup_pack": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _PK, _P, _P, _P, _SZ, _P]),
     "twell_hidden_down": (ctypes.c_int, [_P, _PK, _I64, _I64, _I64, _I32, _I32, _P, _P]),
@@ -321,6 +323,28 @@ def ffn_forward(x, Wg, WuT, Wd, T: int, C: int, y=None, workspace=None, ctrl=Non
     cb = _workspace(ctrl, x.device, zeroed=True)
     cp, cn = cb.get(ctrl_bytes(M))
     _check(lib().twell_ffn_forward(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, _stream(x)), "twell_ffn_forward")
+    return y
+
+
+def ffn_forward_timed(x, Wg, WuT, Wd, T: int, C: int, gate_begin, gate_end, y=None, workspace=None, ctrl=None):
+    """twell_ffn_forward_timed: the forward, with two torch.cuda.Event
+    (enable_timing=True) recorded on the current stream around the gate's
+    launches; gate_begin.elapsed_time(gate_end) is then the gate's time."""
+    M, d = x.shape
+    F = Wg.shape[0]
+    args = (_bf16(x, "x", (M, d)), _bf16(Wg, "Wg", (F, d)), _bf16(WuT, "WuT", (F, d)), _bf16(Wd, "Wd", (F, d)))
+    y = _f32_out(y, "y", (M, d), x.device)
+    ws = _workspace(workspace, x.device)
+    wp, wn = ws.get(workspace_bytes(OP_FFN_FORWARD, M, d, F, T, C))
+    cb = _workspace(ctrl, x.device, zeroed=True)
+    cp, cn = cb.get(ctrl_bytes(M))
+    evs = []
+    for ev in (gate_begin, gate_end):
+        if ev.cuda_event == 0:  # torch creates the event on its first record
+            ev.record()
+        evs.append(ctypes.c_void_p(ev.cuda_event))
+    _check(lib().twell_ffn_forward_timed(*args, M, d, F, T, C, _dptr(y), cp, cn, wp, wn, *evs, _stream(x)),
+           "twell_ffn_forward_timed")
     return y
 
 

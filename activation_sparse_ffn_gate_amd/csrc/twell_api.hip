@@ -299,13 +299,26 @@ int hidden_down_impl(const uint16_t* Wd, const twell_packed* in, int64_t M, int6
 // block's flags.
 int splits_for(int64_t M) { return int(std::min<int64_t>(16, std::max<int64_t>(1, 512 / M))); }
 
+// Optional events recorded on the stream right before the gate's launches
+// and right after them (twell_ffn_forward_timed); null: none.
+struct GateEvents {
+  hipEvent_t begin = nullptr, end = nullptr;
+};
+
+int record(hipEvent_t e, hipStream_t s) {
+  return (e == nullptr || hipEventRecord(e, s) == hipSuccess) ? TWELL_OK : TWELL_E_HIP;
+}
+
 int few_rows_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd, int64_t M,
                      int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl, const twell_packed& p,
-                     float* spill, float* part, size_t part_bytes, hipStream_t s) {
+                     float* spill, float* part, size_t part_bytes, hipStream_t s, GateEvents ev = {}) {
   // The gate's K-split partial sums (if it splits) are consumed before the
   // fused kernel writes its partial rows to the same region.
-  int st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill,
-                          part, part_bytes);
+  int st = record(ev.begin, s);
+  if (st == TWELL_OK)
+    st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s, nullptr, spill, part,
+                        part_bytes);
+  if (st == TWELL_OK) st = record(ev.end, s);
   if (st != TWELL_OK) return st;
   twell::FusedArgs a = fused_args(x, WuT, Wd, &p, M, d, F, T, C, y);
   a.spill = spill;
@@ -658,10 +671,9 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
                     true, static_cast<hipStream_t>(stream));
 }
 
-int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
-                      const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
-                      float* y, void* ctrl, size_t ctrl_bytes_, void* workspace, size_t ws_bytes,
-                      void* stream) {
+static int ffn_forward_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                            int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl,
+                            size_t ctrl_bytes_, void* workspace, size_t ws_bytes, void* stream, GateEvents ev) {
   if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
@@ -678,7 +690,7 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     // the partial rows (at most 512 rows of d floats) its split-K region; both
     // are idle on this path.
     return few_rows_forward(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, p, at<float>(workspace, L.h_hi),
-                            at<float>(workspace, L.split), twell::kDenseSplitBytes, s);
+                            at<float>(workspace, L.split), twell::kDenseSplitBytes, s, ev);
   }
   int dev = -1;
   if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
@@ -686,7 +698,9 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
   SideStream* ss = nullptr;
   st = side_stream_locked(dev, &ss);  // before anything is enqueued
   if (st != TWELL_OK) return st;
-  st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
+  st = record(ev.begin, s);
+  if (st == TWELL_OK) st = gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl), s);
+  if (st == TWELL_OK) st = record(ev.end, s);
   if (st != TWELL_OK) return st;
   // fork: the fallback of the overflow rows on the side stream
   if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
@@ -703,6 +717,24 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
     st = fused_impl(x, WuT, Wd, &p, M, d, F, T, C, y, s);
   if (!joined || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return TWELL_E_HIP;
   return st != TWELL_OK ? st : st_fb;
+}
+
+int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                      const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C,
+                      float* y, void* ctrl, size_t ctrl_bytes_, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  return ffn_forward_impl(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, ctrl_bytes_, workspace, ws_bytes, stream, {});
+}
+
+int twell_ffn_forward_timed(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
+                            int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, float* y, void* ctrl,
+                            size_t ctrl_bytes_, void* workspace, size_t ws_bytes, void* gate_begin,
+                            void* gate_end, void* stream) {
+  if (!gate_begin || !gate_end) return TWELL_E_INVALID_ARG;
+  GateEvents ev;
+  ev.begin = static_cast<hipEvent_t>(gate_begin);
+  ev.end = static_cast<hipEvent_t>(gate_end);
+  return ffn_forward_impl(x, Wg, WuT, Wd, M, d, F, T, C, y, ctrl, ctrl_bytes_, workspace, ws_bytes, stream, ev);
 }
 
 int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,

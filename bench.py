@@ -504,10 +504,40 @@ def distinct_units(view, w):
     return int(mark.sum().item())
 
 
+def gate_events(n):
+    """n pairs of timing events for twell_ffn_forward_timed, created (recorded
+    once) before any timed region."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for b, e in ev:
+        b.record()
+        e.record()
+    torch.cuda.synchronize()
+    return ev
+
+
+def gate_in_forward(fwd_timed, steps):
+    """Mean time of the gate's launches inside `steps` back-to-back forwards,
+    from the event pair each twell_ffn_forward_timed call records around them."""
+    import torch
+
+    ev = gate_events(steps)
+    for i in range(steps):
+        fwd_timed(*ev[i])
+    torch.cuda.synchronize()
+    return sum(b.elapsed_time(e) for b, e in ev) / steps
+
+
 def kernel_legs(dev, w, tensors, k_steps, workload, bufs=None):
     """Each component of the forward timed alone with HIP events on its launch
     stream (k_steps back-to-back launches), the dense baselines, and the
-    roofline of the slower of the gate and the up/down step."""
+    roofline of the slower of the gate and the up/down step. The gate's time
+    in the roofline is its time inside the forward: k_steps back-to-back
+    forwards (twell_ffn_forward_timed, the forward's kernels) with HIP events
+    recorded around the gate's launches in each. They are a loop of their own:
+    the two event records between kernels cost about 10 us per forward at
+    M = 4096 (0.201 against 0.211 ms a step), so the headline steps carry none."""
     import numpy as np
     import torch
 
@@ -545,7 +575,14 @@ def kernel_legs(dev, w, tensors, k_steps, workload, bufs=None):
     for fn in [gate, fused, fallback, dense, dense_tl] + ([sliced] if sliced_ok else []):
         fn()
     torch.cuda.synchronize()
-    t_gate = time_loop(gate, k_steps, stream)
+    t_gate_alone = time_loop(gate, k_steps, stream)
+    ws_fwd = buf("ws_fwd", lambda: tw.Workspace(dev))
+    ctrl_fwd = buf("ctrl_fwd", lambda: tw.Workspace(dev, zeroed=True))
+    for _ in range(3):
+        tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C, y=y, workspace=ws_fwd, ctrl=ctrl_fwd)
+    fwd_timed = lambda b, e: tw.ffn_forward_timed(x, Wg, WuT, Wd, w.T, w.C, b, e, y=y,  # noqa: E731
+                                                  workspace=ws_fwd, ctrl=ctrl_fwd)
+    t_gate, gate_calls = gate_in_forward(fwd_timed, k_steps), k_steps
     t_fused = time_loop(fused, k_steps, stream)
     t_sliced = time_loop(sliced, k_steps, stream) if sliced_ok else None
     t_fb = time_loop(fallback, k_steps, stream)
@@ -574,6 +611,8 @@ def kernel_legs(dev, w, tensors, k_steps, workload, bufs=None):
                 "traffic": hbm.get("gate_pack")}
     legs = {
         "gate_pack_ms": round(t_gate, 5),
+        "gate_pack_timing": f"inside the forward: HIP events around the gate's launches in {gate_calls} forward calls",
+        "gate_pack_alone_ms": round(t_gate_alone, 5),
         "gate_pack_tflops": round(gate_tflops, 1),
         "gate_pack_mfma_frac": round(gate_tflops / PEAK_BF16_TFLOPS, 4),
         "gate_pack_hbm_bytes": hbm.get("gate_pack"),

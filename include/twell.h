@@ -185,6 +185,19 @@ int twell_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT
                       float* y, void* ctrl, size_t ctrl_bytes, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* twell_ffn_forward, plus two caller-created HIP events (hipEvent_t passed as
+ * void*, created with timing enabled, owned by the caller) recorded on
+ * `stream` right before the gate's launches and right after them (at most 256
+ * rows: the K-split and packing launches of the small-batch gate), so that
+ * hipEventElapsedTime gives the gate's time inside the forward, next to the
+ * up/down kernels it alternates with. Same kernels, arguments and result as
+ * twell_ffn_forward; M = 0 records nothing. Both events non-null, else
+ * TWELL_E_INVALID_ARG; a failed record gives TWELL_E_HIP. */
+int twell_ffn_forward_timed(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
+                            const uint16_t* Wd, int64_t M, int64_t d, int64_t F, int32_t T,
+                            int32_t C, float* y, void* ctrl, size_t ctrl_bytes, void* workspace,
+                            size_t ws_bytes, void* gate_begin, void* gate_end, void* stream);
+
 /* Allocation-free form of twell_ffn_forward, for callers that cannot allocate
  * device memory (code under HIP graph capture, serving loops that forbid
  * hipMalloc): no workspace or control block is passed. Up to 256 rows (the

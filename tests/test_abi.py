@@ -109,6 +109,11 @@ def test_forward_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws - 256, None) == E_WS
     assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb - 4, FAKE, ws, None) == E_WS
     assert f(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, None, cb, FAKE, ws, None) == E_WS
+    ft = L.twell_ffn_forward_timed  # both events required; then the forward's own checks, before any record
+    assert ft(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws, None, FAKE, None) == E_ARG
+    assert ft(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws, FAKE, None, None) == E_ARG
+    assert ft(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 96, 8, FAKE, FAKE, cb, FAKE, ws, FAKE, FAKE, None) == E_UNSUP
+    assert ft(FAKE, FAKE, FAKE, FAKE, 256, 256, 1024, 64, 8, FAKE, FAKE, cb, FAKE, ws - 256, FAKE, FAKE, None) == E_WS
     d = L.twell_dense_ffn_forward
     dws = tw.workspace_bytes(tw.OP_DENSE_FFN, 256, 256, 1024)
     assert d(FAKE, FAKE, FAKE, FAKE, 256, 256, 1000, FAKE, FAKE, dws, None) == E_UNSUP

@@ -455,6 +455,22 @@ def test_deterministic_and_control_block_reset():
     assert np.array_equal(p1["ovf"], p2["ovf"]) and np.array_equal(p1["counts"], p2["counts"])
 
 
+@pytest.mark.parametrize("name", ["heavytail_small", "few_rows_d768"])
+def test_forward_timed(name):
+    """twell_ffn_forward_timed runs the forward's kernels (large and
+    small-batch paths): the same y bits as twell_ffn_forward, and its two
+    events bracket a non-empty gate."""
+    inp, _, _, _ = small_case(name)
+    w = inp.workload
+    x, Wg, WuT, Wd = dev(inp)
+    y1 = tw.ffn_forward(x, Wg, WuT, Wd, w.T, w.C).cpu().numpy()
+    b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    y2 = tw.ffn_forward_timed(x, Wg, WuT, Wd, w.T, w.C, b, e, y=nan_y(w.M, w.d))
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    assert b.elapsed_time(e) > 0.0
+
+
 # ------------------------------------------------------------------ full sizes
 def _chunked(fn, M, step=2048):
     return np.concatenate([fn(np.arange(s, min(s + step, M))) for s in range(0, M, step)])
