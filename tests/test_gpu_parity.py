@@ -61,6 +61,10 @@ SMALL = {
     "few_rows_cut_spill": scaled(WORKLOADS["sweep_p3pct"], M=24, d=512, F=16384, C=8),
     # the headline's d = 2048 through the small-batch forward and the training path
     "d2048_small": scaled(WORKLOADS["ffn1p5b"], M=200, d=2048, F=1024, mean_nnz=24.0),
+    # The gate's K split (64 tiles of 32 x 128) with ~490 units a row at C = 8:
+    # every row overflows (its tiles' z spilled) and is cut over several
+    # workgroups
+    "split_cut_overflow": scaled(WORKLOADS["sweep_p3pct"], M=24, d=512, F=8192, C=8, mean_nnz=490.0),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
