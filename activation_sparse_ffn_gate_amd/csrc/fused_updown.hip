@@ -169,6 +169,45 @@ constexpr int kWideWaves = 8;
 constexpr int kWideCap = 1024;  // list entries per round
 constexpr int kSplitMinEntries = 384;  // longer rows may be cut into parts
 constexpr int kSplitChunk = 192;       // entries per part at least
+constexpr int kShortDn = 16;           // down-pass step of short rounds
+
+// Down product over list entries lo .. n - 1 of a round (wide kernel): S
+// entries' Wd loads issued at a time, each lane adding h_j Wd[j] into its NQ
+// 4-column groups in list order.
+template <int S, int NQ>
+__device__ __forceinline__ void wide_down(float (&acc)[NQ][4], const int* s_j, const float* s_h, int lo, int n,
+                                          const char* wdb, uint32_t row_bytes, int quads, int w, int lane) {
+  for (int e0 = lo; e0 < n; e0 += S) {
+    const int jv = s_j[min(e0 + min(lane, S - 1), n - 1)];
+    const float hv = s_h[min(e0 + min(lane, S - 1), n - 1)];
+    u32x2_t wd[S][NQ];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const size_t rb = static_cast<size_t>(__builtin_amdgcn_readlane(jv, u)) * row_bytes;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {  // unconditional (column clamped): keeps the waits counted
+        const int q = min((i * kWideWaves + w) * 64 + lane, quads - 1);
+        wd[u][i] = *reinterpret_cast<const u32x2_t*>(wdb + rb + static_cast<uint32_t>(q) * 8u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      if (e0 + u < n) {  // uniform
+        const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), u));
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          if ((i * kWideWaves + w) * 64 < quads) {  // uniform
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              acc[i][2 * q] = fmaf(h, bf16_lo(wd[u][i][q]), acc[i][2 * q]);
+              acc[i][2 * q + 1] = fmaf(h, bf16_hi(wd[u][i][q]), acc[i][2 * q + 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
 
 template <int VEC, int NCH, int UP, int NQ, int DN>
 __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(FusedArgs a) {
@@ -307,37 +346,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void fused_updown_wide_kernel(Fuse
       }
       __syncthreads();
 
-      // Down: the whole list in order, DN entries' loads at a time.
-      for (int e0 = lo; e0 < n; e0 += DN) {
-        const int jv = s_j[min(e0 + min(lane, DN - 1), n - 1)];
-        const float hv = s_h[min(e0 + min(lane, DN - 1), n - 1)];
-        u32x2_t wd[DN][NQ];
-#pragma unroll
-        for (int u = 0; u < DN; ++u) {
-          const size_t rb = static_cast<size_t>(__builtin_amdgcn_readlane(jv, u)) * row_bytes;
-#pragma unroll
-          for (int i = 0; i < NQ; ++i) {
-            const int q = (i * kWideWaves + w) * 64 + lane;
-            if (q < quads) wd[u][i] = *reinterpret_cast<const u32x2_t*>(wdb + rb + static_cast<uint32_t>(q) * 8u);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < DN; ++u) {
-          if (e0 + u < n) {  // uniform
-            const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), u));
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-              if ((i * kWideWaves + w) * 64 < quads) {  // uniform
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                  acc[i][2 * q] = fmaf(h, bf16_lo(wd[u][i][q]), acc[i][2 * q]);
-                  acc[i][2 * q + 1] = fmaf(h, bf16_hi(wd[u][i][q]), acc[i][2 * q + 1]);
-                }
-              }
-            }
-          }
-        }
-      }
+      // Down: the whole list in order, DN entries' loads at a time, or
+      // kShortDn for a round of at most 4 kShortDn entries (a few-token row),
+      // whose loads past the list would otherwise outnumber its own.
+      if (DN > kShortDn && n - lo <= 4 * kShortDn)  // uniform
+        wide_down<(DN > kShortDn ? kShortDn : DN), NQ>(acc, s_j, s_h, lo, n, wdb, row_bytes, quads, w, lane);
+      else
+        wide_down<DN, NQ>(acc, s_j, s_h, lo, n, wdb, row_bytes, quads, w, lane);
       __syncthreads();  // the list is refilled next round
     }
     gbase += total;
