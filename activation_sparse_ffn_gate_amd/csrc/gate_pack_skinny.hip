@@ -86,8 +86,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = w & 3, kh = w >> 2;  // unit group, K split
-  const int m0 = (blockIdx.x % tiles_m) * kSM;
-  const int n0 = (blockIdx.x / tiles_m) * kSN;
+  // Tile index: workgroups are dispatched round-robin over the 8 XCDs, and
+  // the tiles_m token tiles of one unit tile (consecutive indices) read the
+  // same Wg rows, so with several token tiles each XCD takes a contiguous run
+  // of indices and those reads meet in its L2 instead of each XCD fetching
+  // them again (one token tile shares nothing: dispatch order kept).
+  const int nwg = gridDim.x;
+  const int tix = (tiles_m > 1 && nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int m0 = (tix % tiles_m) * kSM;
+  const int n0 = (tix / tiles_m) * kSN;
   const int r = lane & 31, half = lane >> 5;
 
   f32x16_t acc[RB];
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
     // added in split order as the single launch adds its waves' sums (float4s
     // of rows past M were not stored: they read as zero, those rows never count).
     const float4* src = reinterpret_cast<const float4*>(a.kpart) +
-                        (static_cast<size_t>(blockIdx.x) * kKS * 4 + wn) * 64 * 4 * RB + lane * 4 * RB;
+                        (static_cast<size_t>(tix) * kKS * 4 + wn) * 64 * 4 * RB + lane * 4 * RB;
 #pragma unroll
     for (int b = 0; b < RB; ++b)
 #pragma unroll
