@@ -58,6 +58,30 @@ __device__ __forceinline__ SplitPlan plan_split(bool allowed, int tiles, int nk)
   return {S, tiles * S};
 }
 
+// Output tile and K split of work item `item`. Unsplit, with whole passes of
+// the persistent grid: workgroups are dispatched round-robin over the 8 XCDs,
+// so each XCD takes a contiguous run of every pass's items, walked in groups
+// of kGroupM token tiles (unit tiles within a group): the tiles an XCD runs
+// at once form a block of 8 x 8 that shares its x and weight tiles in that
+// XCD's L2. Otherwise token tiles vary fastest.
+constexpr int kGroupM = 8;
+struct DenseTile {
+  int m0, n0, sp;
+};
+__device__ __forceinline__ DenseTile dense_tile(int item, const SplitPlan& plan, int tiles_m, int tiles_n) {
+  const int G = gridDim.x;
+  if (plan.S == 1 && G % 8 == 0 && plan.items % G == 0 && tiles_m >= kGroupM) {
+    const int pass = item / G, b = item - pass * G;
+    const int lin = pass * G + (b % 8) * (G / 8) + b / 8;
+    const int group = lin / (kGroupM * tiles_n);
+    const int within = lin - group * kGroupM * tiles_n;
+    const int gm = min(kGroupM, tiles_m - group * kGroupM);
+    return {(group * kGroupM + within % gm) * kDM, (within / gm) * kDN, 0};
+  }
+  const int tile = item / plan.S;
+  return {(tile % tiles_m) * kDM, (tile / tiles_m) * kDN, item % plan.S};
+}
+
 // Element (row, column) of float4 q of thread t in a tile's flattened
 // accumulators (flatten below): rows row0 .. row0 + 3 of one column.
 struct PartPos {
@@ -128,10 +152,9 @@ __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
   for (int item = blockIdx.x; item < plan.items; item += gridDim.x) {
-    const int tile = item / plan.S, sp = item % plan.S;
+    const DenseTile dt = dense_tile(item, plan, tiles_m, tiles_n);
+    const int sp = dt.sp, m0 = dt.m0, n0 = dt.n0;
     const int kb = sp * nk / plan.S, ke = (sp + 1) * nk / plan.S;  // this split's K chunks
-    const int m0 = (tile % tiles_m) * kDM;
-    const int n0 = (tile / tiles_m) * kDN;
     const uint16_t *pa[2], *pg[2], *pu[2];
     bool va[2], vb[2];
 #pragma unroll
@@ -251,10 +274,9 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
 
   for (int item = blockIdx.x; item < plan.items; item += gridDim.x) {
-    const int tile = item / plan.S, sp = item % plan.S;
+    const DenseTile dt = dense_tile(item, plan, tiles_m, tiles_n);
+    const int sp = dt.sp, m0 = dt.m0, n0 = dt.n0;
     const int kb = sp * nk / plan.S, ke = (sp + 1) * nk / plan.S;
-    const int m0 = (tile % tiles_m) * kDM;
-    const int n0 = (tile / tiles_m) * kDN;
     const uint16_t* pa[kNA][2];
     bool va[2];
 #pragma unroll
