@@ -210,6 +210,36 @@ def pin_zero_density(o):
     assert np.all(o.ffn_from_twell(p, x, Wg, WuT, Wd) == 0)
 
 
+def pin_one_active_unit(o):
+    # One active gate unit per row: x_r = e_0 + e_{1+j(r)} and Wg_j = -0.5 e_0 +
+    # e_{1+j} give z[r, j] = 0.5 for j = j(r) and -0.5 elsewhere, so
+    # y_r = 0.5 (x_r . WuT_j(r)) Wd_j(r) in closed form, and the packing holds
+    # exactly that unit.
+    rng = np.random.default_rng(17)
+    M, F, T, C = 6, 16, 8, 2
+    d = F + 8
+    jr = rng.permutation(F)[:M]
+    xf = np.zeros((M, d))
+    xf[:, 0] = 1.0
+    xf[np.arange(M), 1 + jr] = 1.0
+    gf = np.zeros((F, d))
+    gf[:, 0] = -0.5
+    gf[np.arange(F), 1 + np.arange(F)] = 1.0
+    x, Wg = bf(xf), bf(gf)
+    WuT, Wd = rand_bf16(rng, (F, d)), rand_bf16(rng, (F, d))
+    U, D = o_ref_decode(WuT), o_ref_decode(Wd)
+    want = np.stack([0.5 * (xf[r] @ U[jr[r]]) * D[jr[r]] for r in range(M)])
+    assert rel(o.dense_gated_ffn(x, Wg, WuT, Wd), want) < 1e-12
+    Z = o.gate_preactivations(x, Wg)
+    p = o.pack_twell(Z.astype(np.float32), T=T, C=C)
+    for r in range(M):
+        t = int(jr[r]) // T
+        assert p.counts[r].tolist() == [1 if k == t else 0 for k in range(F // T)]
+        assert int(p.idx[r, t, 0]) == int(jr[r]) % T and float(p.vals[r, t, 0]) == 0.5
+    assert len(p.ovf) == 0
+    assert rel(o.ffn_from_twell(p, x, Wg, WuT, Wd), want) < 1e-12
+
+
 def _csr_reference(Z, T, C):
     """Per-tile slices of each CSR row of ReLU(Z) (scipy keeps sorted columns)."""
     A = sps.csr_matrix(np.maximum(Z, 0))
@@ -485,7 +515,7 @@ def pin_hidden_ffn_equals_dense(o):
 
 PINS = [
     pin_decode, pin_hand_example, pin_integer_bruteforce, pin_relu_identity, pin_all_active,
-    pin_zero_density, pin_pack_csr, pin_pack_rowwise_ell, pin_pack_strict, pin_overflow_boundary,
+    pin_zero_density, pin_one_active_unit, pin_pack_csr, pin_pack_rowwise_ell, pin_pack_strict, pin_overflow_boundary,
     pin_sparse_equals_dense, pin_unpack_roundtrip, pin_column_rms,
     pin_column_activity, pin_live_layout, pin_compact_rows, pin_compaction_keeps_ffn,
     pin_backward_hand_example, pin_backward_finite_difference, pin_hybrid_pack,
