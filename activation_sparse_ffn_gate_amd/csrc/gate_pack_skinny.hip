@@ -284,10 +284,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void gate_pack_skinny_kernel(GateAr
     if (tile < nT) {
       const uint32_t row_slots = static_cast<uint32_t>(nT * C);
       const uint32_t ulocal = static_cast<uint32_t>(wt * 32 + r);  // index inside the tile
+      // Uniform skips: registers whose rows all lie past M, and the spill when
+      // no token of the tile overflows (the common case).
+      const bool spill_any = a.spill != nullptr && __ballot(lane < kSM && tot > C) != 0;
       static_for<0, 16 * RB>([&](auto I) {
         constexpr int b = decltype(I)::value / 16, v = decltype(I)::value % 16;
         constexpr int t_lo = 32 * b + acc_row(v, 0), t_hi = 32 * b + acc_row(v, 1);
-        if (a.spill != nullptr) {  // every z of a (token, tile) that overflows, active or not
+        if (m0 + t_lo >= a.M) return;  // t_lo < t_hi: both rows past M
+        if (spill_any) {  // every z of a (token, tile) that overflows, active or not
           const int t_own = half ? __builtin_amdgcn_readlane(tot, t_hi) : __builtin_amdgcn_readlane(tot, t_lo);
           const int row = m0 + 32 * b + acc_row(v, half);
           if (t_own > C && row < a.M)
