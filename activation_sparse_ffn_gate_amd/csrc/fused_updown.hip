@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void fused_updown_kernel(FusedArgs a) {
 //         x, same reduction) and leaves h_j = g_j * u_j in the list;
 //   down: wave w, lane l owns the 4-column groups q = 64 w + l (+ 64 kWideWaves
 //         i); every wave walks the whole list in order, DN units' Wd loads in
-//         flight at a time, and adds h_j * Wd[j] to its columns.
+//         flight at a time (kShortDn for a round of a few-token row), and adds
+//         h_j * Wd[j] to its columns.
 // A wave reads a round's entries with one LDS load, lane u holding entry u,
 // and takes each unit's index and value from lane u with v_readlane.
 // Every product and every per-column sum is taken in the same order as in the
