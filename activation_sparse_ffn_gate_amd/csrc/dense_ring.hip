@@ -1,0 +1,350 @@
+// Dense gated FFN on the gate kernel's LDS-DMA ring, for gfx950: the dense
+// baseline (the dense matmuls the pages compare against: tgviewer.app
+// Telegram post, paragraph after "Обучение").
+//
+// Both products are run as C = A B^T with A and B row-major, K contiguous,
+// which is the form the gate kernel's pipeline streams: 256 x 256 output
+// elements per workgroup, 4 waves each owning a 128 x 128 quarter in 16
+// accumulator blocks of v_mfma_f32_32x32x16_bf16 (256 AGPRs), K in 32-wide
+// chunks through a 5-stage LDS ring filled by global_load_lds four chunks
+// ahead, with the same pinned order of MFMAs, fragment reads and DMAs.
+//
+// Gated up: A = x, and the 256 B rows of a tile are 64 Wg rows, the same 64
+// units' WuT rows, then the next 64 units' Wg and WuT rows. Wave (wm, wn) then
+// holds z of 64 units in its accumulator blocks 0-1 and u of the same units,
+// lane for lane, in blocks 2-3, so h = ReLU(z) * u is formed in registers and
+// stored as bf16 (rounded to nearest even). A tile covers 256 tokens x 128
+// units and reads one x tile for both products.
+//
+// Down: y = h Wd, and Wd is [F, d] with d contiguous while the MFMA wants 8
+// consecutive k (= F) values per lane. The call first writes Wd^T ([d, F],
+// 2 F d bytes, about 8 us at the 1.5B shape) into the workspace; the product
+// is then A = h, B = Wd^T. When there are fewer output tiles than CUs the K
+// range is cut into S splits: split 0 stores into y, split s > 0 into partial
+// s of the workspace, and a last launch adds the partials to y in split
+// order (the sum order is fixed).
+#include <algorithm>
+
+#include "twell_device.hpp"
+#include "twell_internal.hpp"
+
+namespace twell {
+namespace {
+
+constexpr int kRM = 256;  // A rows per workgroup tile
+constexpr int kRN = 256;  // B rows per workgroup tile
+constexpr int kRK = 32;   // K chunk per LDS stage
+constexpr int kRStages = 5;
+constexpr int kRAhead = kRStages - 1;
+constexpr int kRTileBytes = 256 * kRK * 2;
+constexpr int kRStageBytes = 2 * kRTileBytes;
+constexpr int kRDma = 8;          // global_load_lds per thread per stage (4 for A, 4 for B)
+constexpr int kMinChunks = 8;     // K chunks per split at least (the pipeline's prologue and drain)
+constexpr int kCUs = 256;
+
+enum RingMode { kGatedUp = 0, kDown = 1 };
+
+struct RingArgs {
+  const uint16_t* a;   // A rows [rows_a, K]
+  const uint16_t* b0;  // B rows [rows_b, K] (gated up: Wg)
+  const uint16_t* b1;  // gated up: WuT; down: unused
+  int rows_a, rows_b, K;
+  int S;               // K splits
+  int tiles_m, tiles_n;
+  uint16_t* h;         // gated up: h [rows_a, rows_b] bf16
+  float* y;            // down: y [rows_a, rows_b] fp32 (split 0)
+  float* part;         // down: partial s at part + (s - 1) * rows_a * rows_b
+};
+
+template <int kMode>
+__global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRStages * kRStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  constexpr int kTileN = kMode == kGatedUp ? 128 : 256;  // output columns per tile
+
+  // Work item -> (split, tile): splits vary slowest. Each XCD (workgroups
+  // b with the same b % 8) takes a contiguous run of items, walked in groups
+  // of 8 token tiles, so the tiles an XCD runs at once share A and B rows in
+  // its L2.
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int lin = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + (b / 8) : b;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int sp = lin / tiles;
+  const int t = lin - sp * tiles;
+  constexpr int kGroupM = 8;
+  const int group = t / (kGroupM * a.tiles_n);
+  const int gm = min(kGroupM, a.tiles_m - group * kGroupM);
+  const int within = t - group * kGroupM * a.tiles_n;
+  const int m0 = (group * kGroupM + within % gm) * kRM;
+  const int n0 = (within / gm) * kTileN;
+
+  const int nkt = a.K / kRK;
+  const int c0 = sp * nkt / a.S, c1 = (sp + 1) * nkt / a.S;
+  const int nk = c1 - c0;
+
+  // DMA addressing as in the gate kernel: wave w fills the 16-row blocks
+  // 4w .. 4w+3 of each operand tile; lane l lands on row l / 4 at physical
+  // piece l % 4. Rows past the matrix read a valid row; their results are
+  // discarded. A 32-bit per-lane byte offset from a wave-uniform base.
+  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (w * 4 + i) * 16 + (lane >> 2);
+    const uint32_t lp = static_cast<uint32_t>((lane & 3) ^ lds_swz(row)) * 16u;
+    oa[i] = static_cast<uint32_t>(min(m0 + row, a.rows_a - 1)) * row_bytes + lp;
+    // gated up: B rows 64g .. 64g+63 are Wg (g even) or WuT (g odd) rows of
+    // units n0 + 64 (g / 2) + 0..63, and wave w's blocks all lie in g = w
+    const int brow = kMode == kGatedUp ? n0 + (w >> 1) * 64 + i * 16 + (lane >> 2) : n0 + row;
+    ob[i] = static_cast<uint32_t>(min(brow, a.rows_b - 1)) * row_bytes + lp;
+  }
+  const char* abase = reinterpret_cast<const char*>(a.a) + static_cast<size_t>(c0) * kRK * 2;
+  const char* bbase = reinterpret_cast<const char*>((kMode == kGatedUp && (w & 1)) ? a.b1 : a.b0) +
+                      static_cast<size_t>(c0) * kRK * 2;
+  auto dma = [&](int j, int buf, int k0) {
+    uint8_t* st = smem + buf * kRStageBytes + w * 4 * 1024;
+    if (j < 4) dma16(reinterpret_cast<const uint16_t*>(abase + k0 * 2 + oa[j]), st + j * 1024);
+    else dma16(reinterpret_cast<const uint16_t*>(bbase + k0 * 2 + ob[j - 4]), st + kRTileBytes + (j - 4) * 1024);
+  };
+  auto issue = [&](int buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < kRDma; ++j) dma(j, buf, k0);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+
+  struct Frags {
+    u32x4_t a[4], b[4];
+  };
+  auto load_frags = [&](Frags& f, int buf, int ks) {
+    const uint8_t* As = smem + buf * kRStageBytes;
+    const uint8_t* Bs = As + kRTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.a[i] = lds_frag(As, wm * 128 + i * 32, ks, lane);
+      f.b[i] = lds_frag(Bs, wn * 128 + i * 32, ks, lane);
+    }
+  };
+  // One k step: 16 MFMAs; a fragment read of the next step after each of the
+  // first 8, one DMA of a later chunk after every other one of the last 8.
+  auto step = [&](auto kDma0, const Frags& cur, Frags& nxt, int nbuf, int nks, int dbuf, int dk0) {
+    constexpr int d0 = decltype(kDma0)::value;
+    const uint8_t* As = smem + nbuf * kRStageBytes;
+    const uint8_t* Bs = As + kRTileBytes;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int mb = i >> 2, nb = i & 3;
+      acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
+      if (i < 8) {
+        if (i & 1) nxt.b[i >> 1] = lds_frag(Bs, wn * 128 + (i >> 1) * 32, nks, lane);
+        else nxt.a[i >> 1] = lds_frag(As, wm * 128 + (i >> 1) * 32, nks, lane);
+      } else if constexpr (d0 >= 0) {
+        if ((i & 1) == 0) dma(d0 + ((i - 8) >> 1), dbuf, dk0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_32x32x16(f.a[mb], f.b[nb], acc[mb][nb]);
+  };
+  constexpr std::integral_constant<int, -1> no_dma{};
+  constexpr std::integral_constant<int, 0> dma_lo{};
+  constexpr std::integral_constant<int, 4> dma_hi{};
+
+  // The gate kernel's pipeline (nk >= kMinChunks, checked by the host).
+  auto wait_chunks = [](int chunks) {
+    if (chunks >= 2) waitcnt<2 * kRDma, 15>();
+    else if (chunks == 1) waitcnt<kRDma, 15>();
+    else waitcnt<0, 15>();
+  };
+  static_assert(kRAhead == 4, "the batch split below assumes chunks run four ahead");
+#pragma unroll
+  for (int s = 0; s < kRAhead - 1; ++s) issue(s, s * kRK);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma(j, kRAhead - 1, (kRAhead - 1) * kRK);
+  waitcnt<2 * kRDma + 4, 15>();
+  raw_barrier();
+  Frags f0, f1;
+  load_frags(f0, 0, 0);
+  int kt = 0;
+  for (; kt < nk - kRAhead; ++kt) {
+    step(dma_hi, f0, f1, kt % kRStages, 1, (kt + kRAhead - 1) % kRStages, (kt + kRAhead - 1) * kRK);
+    waitcnt<2 * kRDma, 15>();
+    raw_barrier();
+    step(dma_lo, f1, f0, (kt + 1) % kRStages, 0, (kt + kRAhead) % kRStages, (kt + kRAhead) * kRK);
+  }
+  step(dma_hi, f0, f1, kt % kRStages, 1, (kt + kRAhead - 1) % kRStages, (kt + kRAhead - 1) * kRK);
+  wait_chunks(nk - 2 - kt);
+  raw_barrier();
+  step(no_dma, f1, f0, (kt + 1) % kRStages, 0, 0, 0);
+  for (++kt; kt < nk - 1; ++kt) {
+    step(no_dma, f0, f1, kt % kRStages, 1, 0, 0);
+    wait_chunks(nk - 2 - kt);
+    raw_barrier();
+    step(no_dma, f1, f0, (kt + 1) % kRStages, 0, 0, 0);
+  }
+  step(no_dma, f0, f1, (nk - 1) % kRStages, 1, 0, 0);
+  mma(f1);
+
+  // ------------------------------------------------------------- epilogue
+  const int half = lane >> 5, col = lane & 31;
+  const int wrow0 = m0 + wm * 128;
+  if constexpr (kMode == kGatedUp) {
+    const int F = a.rows_b;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wrow0 + mb * 32 + acc_row(v, half);
+        if (row < a.rows_a) {
+          uint16_t* hr = a.h + static_cast<size_t>(row) * F;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int unit = n0 + wn * 64 + nb * 32 + col;
+            if (unit < F) {
+              const float hv = fmaxf(acc[mb][nb][v], 0.f) * acc[mb][nb + 2][v];
+              hr[unit] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+            }
+          }
+        }
+      }
+  } else {
+    const int d = a.rows_b;
+    float* dst = sp == 0 ? a.y : a.part + static_cast<size_t>(sp - 1) * a.rows_a * d;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wrow0 + mb * 32 + acc_row(v, half);
+        if (row < a.rows_a) {
+          float* yr = dst + static_cast<size_t>(row) * d + n0 + wn * 128 + col;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) yr[nb * 32] = acc[mb][nb][v];
+        }
+      }
+  }
+}
+
+// dst [cols, rows] = src [rows, cols]^T for bf16, 64 x 64 tiles through LDS
+// (rows and cols multiples of 64).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
+                                                        uint16_t* __restrict__ dst, int rows, int cols) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows: 16-byte aligned
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 256 * i, r = p >> 3, q = p & 7;
+    *reinterpret_cast<u32x4_t*>(&tile[r][q * 8]) =
+        gload16(src + static_cast<size_t>(r0 + r) * cols + c0 + q * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + 256 * i, c = p >> 3, q = p & 7;
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<uint32_t>(tile[q * 8 + 2 * e][c]) | (static_cast<uint32_t>(tile[q * 8 + 2 * e + 1][c]) << 16);
+    *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(c0 + c) * rows + r0 + q * 8) = v;
+  }
+}
+
+// y += partial 1, then partial 2, ... (S - 1 partials of n floats; n % 4 == 0).
+__global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ y, const float* __restrict__ part,
+                                                           int64_t n, int S) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float4 v = reinterpret_cast<const float4*>(y)[i];
+    for (int s = 1; s < S; ++s) {
+      const float4 p = reinterpret_cast<const float4*>(part + static_cast<size_t>(s - 1) * n)[i];
+      v.x += p.x;
+      v.y += p.y;
+      v.z += p.z;
+      v.w += p.w;
+    }
+    reinterpret_cast<float4*>(y)[i] = v;
+  }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int dense_ring_splits(int64_t M, int64_t d, int64_t F) {
+  const int64_t tiles = ceil_div(M, kRM) * (d / kRN);
+  const int64_t by_k = (F / kRK) / kMinChunks;
+  int64_t S = tiles >= kCUs ? 1 : kCUs / tiles;
+  S = std::min<int64_t>(S, by_k);
+  return static_cast<int>(std::max<int64_t>(S, 1));
+}
+
+bool dense_ring_supports(int64_t M, int64_t d, int64_t F) {
+  const int64_t lim = int64_t(1) << 31;  // 32-bit per-lane byte offsets
+  return M >= 1 && d % kRN == 0 && d / kRK >= kMinChunks && F % 64 == 0 && F / kRK >= kMinChunks &&
+         M * d * 2 < lim && F * d * 2 < lim && M * F * 2 < lim;
+}
+
+size_t dense_ring_bytes(int64_t M, int64_t d, int64_t F) {
+  const size_t wdt = align256(size_t(F) * size_t(d) * 2);
+  return wdt + align256(size_t(dense_ring_splits(M, d, F) - 1) * size_t(M) * size_t(d) * 4);
+}
+
+hipError_t launch_dense_ring(const DenseArgs& da, void* ring_ws, hipStream_t s) {
+  const int M = da.M, d = da.d, F = da.F;
+  uint16_t* wdt = static_cast<uint16_t*>(ring_ws);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ring_ws) + align256(size_t(F) * size_t(d) * 2));
+
+  transpose_kernel<<<dim3(F / 64, d / 64), dim3(256), 0, s>>>(da.Wd, wdt, F, d);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  RingArgs up{};
+  up.a = da.x;
+  up.b0 = da.Wg;
+  up.b1 = da.WuT;
+  up.rows_a = M;
+  up.rows_b = F;
+  up.K = d;
+  up.S = 1;
+  up.tiles_m = static_cast<int>(ceil_div(M, kRM));
+  up.tiles_n = static_cast<int>(ceil_div(F, 128));
+  up.h = da.h_hi;
+  ring_kernel<kGatedUp><<<dim3(up.tiles_m * up.tiles_n), dim3(256), 0, s>>>(up);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  RingArgs dn{};
+  dn.a = da.h_hi;
+  dn.b0 = wdt;
+  dn.b1 = wdt;
+  dn.rows_a = M;
+  dn.rows_b = d;
+  dn.K = F;
+  dn.S = dense_ring_splits(M, d, F);
+  dn.tiles_m = up.tiles_m;
+  dn.tiles_n = d / kRN;
+  dn.y = da.y;
+  dn.part = part;
+  ring_kernel<kDown><<<dim3(dn.tiles_m * dn.tiles_n * dn.S), dim3(256), 0, s>>>(dn);
+  e = hipGetLastError();
+  if (e != hipSuccess || dn.S == 1) return e;
+  add_partials_kernel<<<dim3(2048), dim3(256), 0, s>>>(da.y, part, int64_t(M) * d, dn.S);
+  return hipGetLastError();
+}
+
+}  // namespace twell

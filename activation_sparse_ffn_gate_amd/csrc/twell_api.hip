@@ -18,6 +18,7 @@ constexpr int64_t kMaxF = int64_t(1) << 24;
 struct Layout {
   size_t vals = 0, idx = 0, counts = 0, ovf_rows = 0, n_ovf = 0, h_hi = 0, h_lo = 0, part = 0;
   size_t split = 0;  // the split-K fallback's partial tiles
+  size_t ring = 0;   // the dense baseline's Wd^T and split partials
   size_t total = 0;
 };
 
@@ -29,7 +30,7 @@ uint32_t* row_counters(void* ctrl, int64_t M) {
 }
 
 // Offsets inside the workspace of each operation (all 256-byte aligned).
-Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
+Layout layout(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -78,6 +79,7 @@ Layout layout(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C) {
       break;
     case TWELL_OP_DENSE_FFN:
       L.h_hi = take(m * f * 2);
+      if (twell::dense_ring_supports(M, d, F)) L.ring = take(twell::dense_ring_bytes(M, d, F));
       break;
     case TWELL_OP_DENSE_FALLBACK:
       L.h_hi = take(m * f * 2);
@@ -112,8 +114,8 @@ int check_gate_offsets(int64_t M, int64_t d, int64_t F, int32_t T, int32_t C) {
   return TWELL_OK;
 }
 
-int check_ws(int32_t op, int64_t M, int64_t F, int32_t T, int32_t C, void* ws, size_t ws_bytes) {
-  const Layout L = layout(op, M, F, T, C);
+int check_ws(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C, void* ws, size_t ws_bytes) {
+  const Layout L = layout(op, M, d, F, T, C);
   if (L.total == 0) return TWELL_OK;
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.total)
     return TWELL_E_WORKSPACE;
@@ -647,9 +649,9 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
   if (st == TWELL_OK && !twell::sliced_supports(d, F)) st = TWELL_E_UNSUPPORTED;
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_SLICED_UPDOWN, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_SLICED_UPDOWN, M, d, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
-  const Layout L = layout(TWELL_OP_SLICED_UPDOWN, M, F, T, C);
+  const Layout L = layout(TWELL_OP_SLICED_UPDOWN, M, d, F, T, C);
   return sliced_impl(x, WuT, Wd, in, M, d, F, T, C, at<uint8_t>(workspace, L.part), y,
                      static_cast<hipStream_t>(stream));
 }
@@ -663,9 +665,9 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
   int st = check_dims(M, d, F);
   if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FALLBACK, M, d, F, 0, 0, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
-  const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, F, 0, 0);
+  const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, d, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, in->ovf_rows, in->n_ovf, at<uint16_t>(workspace, L.h_hi),
                     at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
                     true, static_cast<hipStream_t>(stream));
@@ -679,11 +681,11 @@ static int ffn_forward_impl(const uint16_t* x, const uint16_t* Wg, const uint16_
   if (st == TWELL_OK) st = check_tc(F, T, C);
   if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, d, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   if (M == 0) return TWELL_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Layout L = layout(TWELL_OP_FFN_FORWARD, M, F, T, C);
+  const Layout L = layout(TWELL_OP_FFN_FORWARD, M, d, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
   if (M <= twell::kFewRows) {
     // The spill (M F floats) takes the fallback's hidden pair (2 M F bf16) and
@@ -797,11 +799,11 @@ int twell_ffn_forward_gateup(const uint16_t* x, const uint16_t* Wg, const uint16
   if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK && !twell::sliced_supports(d, F)) st = TWELL_E_UNSUPPORTED;
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD_GATEUP, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD_GATEUP, M, d, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   if (M == 0) return TWELL_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Layout L = layout(TWELL_OP_FFN_FORWARD_GATEUP, M, F, T, C);
+  const Layout L = layout(TWELL_OP_FFN_FORWARD_GATEUP, M, d, F, T, C);
   const twell_packed p = packed_in_ws(workspace, L);
   int dev = -1;
   if (stream_device(s, &dev) != TWELL_OK) return TWELL_E_HIP;
@@ -828,9 +830,22 @@ int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_
   if (!Wg || !WuT || !Wd || (M != 0 && (!x || !y))) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK && F % 64 != 0) st = TWELL_E_UNSUPPORTED;
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FFN, M, F, 0, 0, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_DENSE_FFN, M, d, F, 0, 0, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
-  const Layout L = layout(TWELL_OP_DENSE_FFN, M, F, 0, 0);
+  const Layout L = layout(TWELL_OP_DENSE_FFN, M, d, F, 0, 0);
+  if (M != 0 && twell::dense_ring_supports(M, d, F)) {
+    twell::DenseArgs a{};
+    a.x = x;
+    a.Wg = Wg;
+    a.WuT = WuT;
+    a.Wd = Wd;
+    a.M = int(M);
+    a.d = int(d);
+    a.F = int(F);
+    a.h_hi = at<uint16_t>(workspace, L.h_hi);
+    a.y = y;
+    return hip_status(twell::launch_dense_ring(a, at<uint8_t>(workspace, L.ring), static_cast<hipStream_t>(stream)));
+  }
   return dense_impl(x, Wg, WuT, Wd, M, d, F, nullptr, nullptr, at<uint16_t>(workspace, L.h_hi),
                     nullptr, y, nullptr, false, static_cast<hipStream_t>(stream));
 }
@@ -843,10 +858,10 @@ int twell_column_activity(const uint16_t* x, const uint16_t* Wg, int64_t M, int6
   if (st == TWELL_OK) st = check_tc(F, T, C);
   if (st == TWELL_OK) st = check_gate_offsets(M, d, F, T, C);
   if (st == TWELL_OK) st = check_ctrl(M, ctrl, ctrl_bytes_);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_COLUMN_ACTIVITY, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_COLUMN_ACTIVITY, M, d, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
   if (M == 0) return TWELL_OK;
-  const twell_packed p = packed_in_ws(workspace, layout(TWELL_OP_COLUMN_ACTIVITY, M, F, T, C));
+  const twell_packed p = packed_in_ws(workspace, layout(TWELL_OP_COLUMN_ACTIVITY, M, d, F, T, C));
   return gate_pack_impl(x, Wg, M, d, F, T, C, &p, nullptr, static_cast<uint32_t*>(ctrl),
                         static_cast<hipStream_t>(stream), active_bits);
 }
@@ -893,7 +908,7 @@ size_t twell_workspace_bytes(int32_t op, int64_t M, int64_t d, int64_t F, int32_
   } else {
     return 0;
   }
-  return layout(op, M, F, T, C).total;
+  return layout(op, M, d, F, T, C).total;
 }
 
 size_t twell_ctrl_bytes(int64_t M) {
@@ -906,9 +921,9 @@ int twell_packed_view(void* workspace, size_t ws_bytes, int64_t M, int64_t d, in
   if (!out) return TWELL_E_INVALID_ARG;
   int st = check_dims(M, d, F);
   if (st == TWELL_OK) st = check_tc(F, T, C);
-  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, F, T, C, workspace, ws_bytes);
+  if (st == TWELL_OK) st = check_ws(TWELL_OP_FFN_FORWARD, M, d, F, T, C, workspace, ws_bytes);
   if (st != TWELL_OK) return st;
-  *out = packed_in_ws(workspace, layout(TWELL_OP_FFN_FORWARD, M, F, T, C));
+  *out = packed_in_ws(workspace, layout(TWELL_OP_FFN_FORWARD, M, d, F, T, C));
   return TWELL_OK;
 }
 

@@ -176,6 +176,14 @@ hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 hipError_t launch_gateup_pack(const GateArgs& a, hipStream_t s);
 hipError_t launch_hidden_down(const SlicedArgs& a, hipStream_t s);
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
+
+// Dense baseline on the gate kernel's LDS-DMA ring (rows 0..M-1, bf16 h):
+// whether the shape fits its 32-bit offsets, the K splits of its down
+// product, and the workspace it needs (Wd^T, then the partials of splits 1..).
+bool dense_ring_supports(int64_t M, int64_t d, int64_t F);
+int dense_ring_splits(int64_t M, int64_t d, int64_t F);
+size_t dense_ring_bytes(int64_t M, int64_t d, int64_t F);
+hipError_t launch_dense_ring(const DenseArgs& a, void* ring_ws, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);
 
 bool fused_supports_d(int d);

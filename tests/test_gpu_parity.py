@@ -392,6 +392,34 @@ def test_dense_baseline(name):
     assert rel < 5e-3  # bf16 rounding of h gives ~1.5e-3 by design; reported, not gated at 1e-3
 
 
+# Shapes for the dense baseline's tiling: 256-token x 128-unit gated-up tiles
+# and 256 x 256 down tiles whose K range is split when there are fewer tiles
+# than CUs (S = 1, 4, 5, 7, 8 below), ragged token counts, F % 128 == 64.
+DENSE_SHAPES = {
+    "one_token_s8": scaled(WORKLOADS["ffn1p5b"], M=1, d=512, F=2048),
+    "ragged_f1088_s4": scaled(WORKLOADS["ffn1p5b"], M=300, d=256, F=1088, T=64),
+    "d768_s5": scaled(WORKLOADS["ffn1p5b"], M=600, d=768, F=1280),
+    "d1024_s7": scaled(WORKLOADS["ffn1p5b"], M=2100, d=1024, F=4096),
+    "unsplit_d4096": scaled(WORKLOADS["ffn1p5b"], M=4100, d=4096, F=512),
+}
+
+
+@pytest.mark.parametrize("name", list(DENSE_SHAPES))
+def test_dense_baseline_shapes(name):
+    inp = make_inputs(DENSE_SHAPES[name])
+    w = inp.workload
+    Y = O.dense_gated_ffn(inp.x, inp.Wg, inp.WuT, inp.Wd)
+    args = dev(inp)
+    y = tw.dense_ffn_forward(*args, y=nan_y(w.M, w.d))
+    again = tw.dense_ffn_forward(*args, y=nan_y(w.M, w.d))
+    y, again = y.cpu().numpy(), again.cpu().numpy()
+    assert np.isfinite(y).all()
+    assert np.array_equal(y.view(np.uint32), again.view(np.uint32))  # fixed sum order
+    rel, mx, mref = y_errors(y, Y)
+    print(f"{name}: dense baseline rel L2 {rel:.2e}, max {mx:.2e} of {mref:.2e}")
+    assert rel < 5e-3 and mx <= 2e-2 * mref
+
+
 # ------------------------------------------------------------------ edge cases
 def _edge_inputs(M, d, F, bias, seed=5):
     rng = np.random.default_rng(seed)
