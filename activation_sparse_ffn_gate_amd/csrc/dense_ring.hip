@@ -200,84 +200,131 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
   mma(f1);
 
   // ------------------------------------------------------------- epilogue
+  // The tile goes out through the idle ring so every global store is a whole
+  // 16-byte piece of a row (a store from the accumulator layout would write
+  // 2 or 4 bytes per lane).
   const int half = lane >> 5, col = lane & 31;
-  const int wrow0 = m0 + wm * 128;
+  waitcnt<63, 0>();
+  raw_barrier();  // every wave is past its last fragment reads of the ring
   if constexpr (kMode == kGatedUp) {
-    const int F = a.rows_b;
+    // h of the 256 x 128 tile as bf16 rows of 128 (+8 padding) units
+    constexpr int kHS = 128 + 8;
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wrow0 + mb * 32 + acc_row(v, half);
-        if (row < a.rows_a) {
-          uint16_t* hr = a.h + static_cast<size_t>(row) * F;
+        const int r = wm * 128 + mb * 32 + acc_row(v, half);
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int unit = n0 + wn * 64 + nb * 32 + col;
-            if (unit < F) {
-              const float hv = fmaxf(acc[mb][nb][v], 0.f) * acc[mb][nb + 2][v];
-              hr[unit] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
-            }
-          }
+        for (int nb = 0; nb < 2; ++nb) {
+          const float hv = fmaxf(acc[mb][nb][v], 0.f) * acc[mb][nb + 2][v];
+          hs[r * kHS + wn * 64 + nb * 32 + col] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
         }
       }
+    waitcnt<63, 0>();
+    raw_barrier();
+    const int F = a.rows_b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int piece = i * 256 + tid, r = piece >> 4, p = piece & 15;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hs + r * kHS + p * 8);
+      if (m0 + r < a.rows_a && n0 + p * 8 < F)
+        *reinterpret_cast<u32x4_t*>(a.h + static_cast<size_t>(m0 + r) * F + n0 + p * 8) = v;
+    }
   } else {
+    // y in two passes of 128 rows (the waves with wm == pass write theirs),
+    // fp32 rows of 256 (+8 padding) columns
+    constexpr int kYS = 256 + 8;
+    float* ys = reinterpret_cast<float*>(smem);
     const int d = a.rows_b;
     float* dst = sp == 0 ? a.y : a.part + static_cast<size_t>(sp - 1) * a.rows_a * d;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wrow0 + mb * 32 + acc_row(v, half);
-        if (row < a.rows_a) {
-          float* yr = dst + static_cast<size_t>(row) * d + n0 + wn * 128 + col;
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) yr[nb * 32] = acc[mb][nb][v];
-        }
+          for (int v = 0; v < 16; ++v) {
+            const int r = mb * 32 + acc_row(v, half);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) ys[r * kYS + wn * 128 + nb * 32 + col] = acc[mb][nb][v];
+          }
       }
+      waitcnt<63, 0>();
+      raw_barrier();
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int piece = i * 256 + tid, r = piece >> 6, p = piece & 63;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ys + r * kYS + p * 4);
+        const int row = m0 + pass * 128 + r;
+        if (row < a.rows_a) *reinterpret_cast<f32x4_t*>(dst + static_cast<size_t>(row) * d + n0 + p * 4) = v;
+      }
+      waitcnt<63, 0>();
+      raw_barrier();  // reads done before the next pass writes
+    }
   }
 }
 
 // dst [cols, rows] = src [rows, cols]^T for bf16, 64 x 64 tiles through LDS
-// (rows and cols multiples of 64).
+// (rows and cols multiples of 64). Thread t loads 8 columns of the row pair
+// 2 (t / 8), 2 (t / 8) + 1 and writes each column's two values as one 32-bit
+// word of the transposed tile, so a 16-byte read there is 8 consecutive rows
+// of one column.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
                                                         uint16_t* __restrict__ dst, int rows, int cols) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows: 16-byte aligned
+  constexpr int kTS = 32 + 4;  // 32-bit words per transposed row (16-byte aligned)
+  __shared__ __attribute__((aligned(16))) uint32_t tt[64 * kTS];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
+  {
+    const int rp = tid >> 3, q = tid & 7;
+    const u32x4_t lo = gload16(src + static_cast<size_t>(r0 + 2 * rp) * cols + c0 + q * 8);
+    const u32x4_t hi = gload16(src + static_cast<size_t>(r0 + 2 * rp + 1) * cols + c0 + q * 8);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + 256 * i, r = p >> 3, q = p & 7;
-    *reinterpret_cast<u32x4_t*>(&tile[r][q * 8]) =
-        gload16(src + static_cast<size_t>(r0 + r) * cols + c0 + q * 8);
+    for (int e = 0; e < 4; ++e) {
+      tt[(q * 8 + 2 * e) * kTS + rp] = (lo[e] & 0xFFFFu) | (hi[e] << 16);
+      tt[(q * 8 + 2 * e + 1) * kTS + rp] = (lo[e] >> 16) | (hi[e] & 0xFFFF0000u);
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int p = tid + 256 * i, c = p >> 3, q = p & 7;
-    u32x4_t v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = static_cast<uint32_t>(tile[q * 8 + 2 * e][c]) | (static_cast<uint32_t>(tile[q * 8 + 2 * e + 1][c]) << 16);
-    *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(c0 + c) * rows + r0 + q * 8) = v;
+    const int p = tid + 256 * i, c = p >> 3, g = p & 7;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&tt[c * kTS + g * 4]);
+    *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(c0 + c) * rows + r0 + g * 8) = v;
   }
 }
 
 // y += partial 1, then partial 2, ... (S - 1 partials of n floats; n % 4 == 0).
+// Four float4 per thread, all loaded before any is stored.
 __global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ y, const float* __restrict__ part,
                                                            int64_t n, int S) {
   const int64_t n4 = n / 4;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    float4 v = reinterpret_cast<const float4*>(y)[i];
-    for (int s = 1; s < S; ++s) {
-      const float4 p = reinterpret_cast<const float4*>(part + static_cast<size_t>(s - 1) * n)[i];
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+  float4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + 256 * j;
+    v[j] = i < n4 ? reinterpret_cast<const float4*>(y)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int s = 1; s < S; ++s) {
+    const float4* ps = reinterpret_cast<const float4*>(part + static_cast<size_t>(s - 1) * n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = i0 + 256 * j;
+      if (i < n4) {
+        const float4 p = ps[i];
+        v[j].x += p.x;
+        v[j].y += p.y;
+        v[j].z += p.z;
+        v[j].w += p.w;
+      }
     }
-    reinterpret_cast<float4*>(y)[i] = v;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + 256 * j;
+    if (i < n4) reinterpret_cast<float4*>(y)[i] = v[j];
   }
 }
 
@@ -343,7 +390,8 @@ hipError_t launch_dense_ring(const DenseArgs& da, void* ring_ws, hipStream_t s) 
   ring_kernel<kDown><<<dim3(dn.tiles_m * dn.tiles_n * dn.S), dim3(256), 0, s>>>(dn);
   e = hipGetLastError();
   if (e != hipSuccess || dn.S == 1) return e;
-  add_partials_kernel<<<dim3(2048), dim3(256), 0, s>>>(da.y, part, int64_t(M) * d, dn.S);
+  const int64_t n = int64_t(M) * d;
+  add_partials_kernel<<<dim3(static_cast<unsigned>(ceil_div(n / 4, 1024))), dim3(256), 0, s>>>(da.y, part, n, dn.S);
   return hipGetLastError();
 }
 
