@@ -514,7 +514,8 @@ def test_full_size(name):
     checked over the whole layer: the forward's own packing and the bit-exact
     mode's packing both equal the oracle's packing of the bit-exact mode's z,
     every active set against the fp64 pre-activations, and every row of y
-    against the fp64 definition."""
+    against the fp64 definition; then the single-kernel form and the dense
+    baseline on the same layer."""
     inp = make_inputs(WORKLOADS[name])
     w = inp.workload
     print(f"[full] {name} M={w.M} d={w.d} F={w.F} T={w.T} C={w.C}", flush=True)
@@ -553,6 +554,14 @@ def test_full_size(name):
     tw.dense_fallback(x, Wg, WuT, Wd, p, yf)
     rel_f, _ = check_y(yf.cpu().numpy(), Y)
     print(f"[full] {name}: fused form whole-tensor rel L2 {rel_f:.2e}")
+
+    # the dense baseline on the same layer (bf16 hidden: its error is reported
+    # and loosely bounded, as in the small cases)
+    yd = tw.dense_ffn_forward(x, Wg, WuT, Wd, y=nan_y(w.M, w.d)).cpu().numpy()
+    assert np.isfinite(yd).all()
+    rel_d, mx_d, mref_d = y_errors(yd, Y)
+    print(f"[full] {name}: dense baseline whole-tensor rel L2 {rel_d:.2e}")
+    assert rel_d < 5e-3 and mx_d <= 2e-2 * mref_d
 
 
 @pytest.mark.parametrize("name", ["ffn1p5b", "ffn1p5b_heavytail"])
