@@ -401,6 +401,10 @@ DENSE_SHAPES = {
     "d768_s5": scaled(WORKLOADS["ffn1p5b"], M=600, d=768, F=1280),
     "d1024_s7": scaled(WORKLOADS["ffn1p5b"], M=2100, d=1024, F=4096),
     "unsplit_d4096": scaled(WORKLOADS["ffn1p5b"], M=4100, d=4096, F=512),
+    # the largest d the library takes (32 down tiles across, S = 2)
+    "d8192_max": scaled(WORKLOADS["ffn1p5b"], M=300, d=8192, F=512),
+    # F / 32 below the ring's 8 chunks: the register-staged kernels run it
+    "register_staged_f128": scaled(WORKLOADS["ffn1p5b"], M=100, d=256, F=128),
 }
 
 
