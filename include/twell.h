@@ -222,7 +222,10 @@ int twell_ffn_forward_static(const uint16_t* x, const uint16_t* Wg, const uint16
 /* Dense MFMA gated-FFN baseline (the comparator the pages measure against:
  * dense matmuls, tgviewer.app Telegram post, paragraph after "Обучение"):
  * h = ReLU(x Wg^T) ⊙ (x WuT^T) rounded to bf16 and written to the workspace,
- * then y = h Wd in fp32. workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FFN, ...). */
+ * then y = h Wd in fp32. The workspace also receives a transposed copy of Wd
+ * and, when the down product's K range is split across workgroups, the
+ * partial outputs that are added to y in split order (fixed order: two calls
+ * give the same bits). workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FFN, ...). */
 int twell_dense_ffn_forward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
                             const uint16_t* Wd, int64_t M, int64_t d, int64_t F, float* y,
                             void* workspace, size_t ws_bytes, void* stream);
