@@ -140,6 +140,7 @@ template <bool kGather, bool kSplit>
 __global__ __launch_bounds__(256, 2) void gated_up_kernel(DenseArgs a, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 3 * kTile];
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
+  if (kGather && a.ring_min_rows > 0 && R >= a.ring_min_rows) return;  // the ring kernels take this list
   const int tiles_m = (R + kDM - 1) / kDM;
   const int nk = a.d / kDK;
   const SplitPlan plan = plan_split(kGather && a.split_k, tiles_m * tiles_n, nk);
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(256, 2) void down_kernel(DenseArgs a, int tiles_n) 
   constexpr int kStage = (kNA + 1) * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
   const int R = kGather ? min(max(*a.n_rows, 0), a.M) : a.M;
+  if (kGather && a.ring_min_rows > 0 && R >= a.ring_min_rows) return;  // the ring kernels take this list
   const int tiles_m = (R + kDM - 1) / kDM;
   const int nk = a.F / kDK;
   const SplitPlan plan = plan_split(kGather && a.split_k, tiles_m * tiles_n, nk);
@@ -385,6 +387,7 @@ constexpr int kReduceWGs = 2048;  // at most 127 split tiles x 16 units: one uni
 template <bool kSplit>
 __global__ __launch_bounds__(256) void gated_up_reduce_kernel(DenseArgs a, int tiles_n) {
   const int R = min(max(*a.n_rows, 0), a.M);
+  if (a.ring_min_rows > 0 && R >= a.ring_min_rows) return;  // the ring kernels took this list
   const int tiles_m = (R + kDM - 1) / kDM;
   const SplitPlan plan = plan_split(a.split_k, tiles_m * tiles_n, a.d / kDK);
   if (plan.S <= 1) return;
@@ -414,6 +417,7 @@ __global__ __launch_bounds__(256) void gated_up_reduce_kernel(DenseArgs a, int t
 
 __global__ __launch_bounds__(256) void down_reduce_kernel(DenseArgs a, int tiles_n) {
   const int R = min(max(*a.n_rows, 0), a.M);
+  if (a.ring_min_rows > 0 && R >= a.ring_min_rows) return;  // the ring kernels took this list
   const int tiles_m = (R + kDM - 1) / kDM;
   const SplitPlan plan = plan_split(a.split_k, tiles_m * tiles_n, a.F / kDK);
   if (plan.S <= 1) return;
@@ -447,8 +451,11 @@ hipError_t launch_pair(const DenseArgs& a, hipStream_t s) {
     g2 = g2 < kPersistentWGs ? g2 : kPersistentWGs;
   }
   DenseArgs up = a, down = a;
+  hipError_t e = hipSuccess;
+  const bool ring = kGather && kSplit && a.ring_ws != nullptr;
+  if (ring && (e = launch_ring_fallback_up(a, s)) != hipSuccess) return e;
   gated_up_kernel<kGather, kSplit><<<dim3(g1), dim3(256), 0, s>>>(up, tiles_nf);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool split = kGather && a.split_k;  // the product kernels may split K
   if (split) {
@@ -456,6 +463,7 @@ hipError_t launch_pair(const DenseArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (ring && (e = launch_ring_fallback_down(a, s)) != hipSuccess) return e;
   down_kernel<kGather, kSplit><<<dim3(g2), dim3(256), 0, s>>>(down, tiles_nd);
   e = hipGetLastError();
   if (e != hipSuccess || !split) return e;

@@ -45,18 +45,29 @@ constexpr int kCUs = 256;
 enum RingMode { kGatedUp = 0, kDown = 1 };
 
 struct RingArgs {
-  const uint16_t* a;   // A rows [rows_a, K]
+  const uint16_t* a;   // A rows [rows_a, K] (hi/lo down: the hi plane, [rows_a, kwrap])
   const uint16_t* b0;  // B rows [rows_b, K] (gated up: Wg)
   const uint16_t* b1;  // gated up: WuT; down: unused
   int rows_a, rows_b, K;
   int S;               // K splits
   int tiles_m, tiles_n;
-  uint16_t* h;         // gated up: h [rows_a, rows_b] bf16
+  uint16_t* h;         // gated up: h [rows_a, rows_b] bf16 (hi/lo: the hi plane)
+  uint16_t* h_lo;      // hi/lo gated up: the lo plane
+  const uint16_t* a_lo;  // hi/lo down: the lo plane of A
+  int kwrap;           // hi/lo down: F (A and B rows hold F elements, K = 2F)
   float* y;            // down: y [rows_a, rows_b] fp32 (split 0)
   float* part;         // down: partial s at part + (s - 1) * rows_a * rows_b
+  // gathering: list i is token rows[i] (A rows of the gated up, y rows of the
+  // down), i < *n_rows; nothing is done when *n_rows < min_rows
+  const int32_t* rows;
+  const int32_t* n_rows;
+  int min_rows;
 };
 
-template <int kMode>
+// kGather: rows come from a device-side list (S = 1, tiles_m from its
+// length); kHiLo: the hidden is kept as a bf16 pair h ~ hi + lo and the down
+// product runs over K = 2F, the hi plane against Wd^T and then the lo plane.
+template <int kMode, bool kGather = false, bool kHiLo = false>
 __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRStages * kRStageBytes];
 
@@ -66,18 +77,26 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
   const int wm = w >> 1, wn = w & 1;
   constexpr int kTileN = kMode == kGatedUp ? 128 : 256;  // output columns per tile
 
+  int R = a.rows_a, tiles_m = a.tiles_m;
+  if constexpr (kGather) {
+    R = min(max(*a.n_rows, 0), a.rows_a);
+    if (R < a.min_rows || R == 0) return;  // the register-staged kernels take this list
+    tiles_m = (R + kRM - 1) / kRM;
+  }
   // Work item -> (split, tile): splits vary slowest. Each XCD (workgroups
   // b with the same b % 8) takes a contiguous run of items, walked in groups
   // of 8 token tiles, so the tiles an XCD runs at once share A and B rows in
-  // its L2.
-  const int nwg = gridDim.x, b = blockIdx.x;
-  const int lin = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + (b / 8) : b;
-  const int tiles = a.tiles_m * a.tiles_n;
+  // its L2. (Gathering, the grid is sized for the longest list and the
+  // workgroups past this list's items return.)
+  const int tiles = tiles_m * a.tiles_n;
+  const int items = tiles * a.S, b = blockIdx.x;
+  if (b >= items) return;
+  const int lin = (items % 8 == 0) ? (b % 8) * (items / 8) + (b / 8) : b;
   const int sp = lin / tiles;
   const int t = lin - sp * tiles;
   constexpr int kGroupM = 8;
   const int group = t / (kGroupM * a.tiles_n);
-  const int gm = min(kGroupM, a.tiles_m - group * kGroupM);
+  const int gm = min(kGroupM, tiles_m - group * kGroupM);
   const int within = t - group * kGroupM * a.tiles_n;
   const int m0 = (group * kGroupM + within % gm) * kRM;
   const int n0 = (within / gm) * kTileN;
@@ -88,15 +107,18 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
 
   // DMA addressing as in the gate kernel: wave w fills the 16-row blocks
   // 4w .. 4w+3 of each operand tile; lane l lands on row l / 4 at physical
-  // piece l % 4. Rows past the matrix read a valid row; their results are
-  // discarded. A 32-bit per-lane byte offset from a wave-uniform base.
-  const uint32_t row_bytes = static_cast<uint32_t>(a.K) * 2u;
+  // piece l % 4. Rows past the matrix (or the list) read a valid row; their
+  // results are discarded. A 32-bit per-lane byte offset from a wave-uniform
+  // base.
+  const uint32_t row_bytes = static_cast<uint32_t>(kHiLo && kMode == kDown ? a.kwrap : a.K) * 2u;
   uint32_t oa[4], ob[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (w * 4 + i) * 16 + (lane >> 2);
     const uint32_t lp = static_cast<uint32_t>((lane & 3) ^ lds_swz(row)) * 16u;
-    oa[i] = static_cast<uint32_t>(min(m0 + row, a.rows_a - 1)) * row_bytes + lp;
+    int arow = min(m0 + row, R - 1);
+    if constexpr (kGather && kMode == kGatedUp) arow = a.rows[arow];  // x row of list entry arow
+    oa[i] = static_cast<uint32_t>(arow) * row_bytes + lp;
     // gated up: B rows 64g .. 64g+63 are Wg (g even) or WuT (g odd) rows of
     // units n0 + 64 (g / 2) + 0..63, and wave w's blocks all lie in g = w
     const int brow = kMode == kGatedUp ? n0 + (w >> 1) * 64 + i * 16 + (lane >> 2) : n0 + row;
@@ -107,8 +129,18 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
                       static_cast<size_t>(c0) * kRK * 2;
   auto dma = [&](int j, int buf, int k0) {
     uint8_t* st = smem + buf * kRStageBytes + w * 4 * 1024;
-    if (j < 4) dma16(reinterpret_cast<const uint16_t*>(abase + k0 * 2 + oa[j]), st + j * 1024);
-    else dma16(reinterpret_cast<const uint16_t*>(bbase + k0 * 2 + ob[j - 4]), st + kRTileBytes + (j - 4) * 1024);
+    if constexpr (kHiLo && kMode == kDown) {
+      // chunks of the second half read the lo plane against the same Wd^T
+      // columns (F % 32 == 0: no chunk straddles the two halves)
+      const bool lo = k0 >= a.kwrap;
+      const int kk = lo ? k0 - a.kwrap : k0;
+      const char* ab = lo ? reinterpret_cast<const char*>(a.a_lo) : abase;
+      if (j < 4) dma16(reinterpret_cast<const uint16_t*>(ab + kk * 2 + oa[j]), st + j * 1024);
+      else dma16(reinterpret_cast<const uint16_t*>(bbase + kk * 2 + ob[j - 4]), st + kRTileBytes + (j - 4) * 1024);
+    } else {
+      if (j < 4) dma16(reinterpret_cast<const uint16_t*>(abase + k0 * 2 + oa[j]), st + j * 1024);
+      else dma16(reinterpret_cast<const uint16_t*>(bbase + k0 * 2 + ob[j - 4]), st + kRTileBytes + (j - 4) * 1024);
+    }
   };
   auto issue = [&](int buf, int k0) {
 #pragma unroll
@@ -208,7 +240,9 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
   raw_barrier();  // every wave is past its last fragment reads of the ring
   if constexpr (kMode == kGatedUp) {
     // h of the 256 x 128 tile as bf16 rows of 128 (+8 padding) units
+    // (hi/lo: the lo plane, h - hi rounded to bf16, in a second region)
     constexpr int kHS = 128 + 8;
+    constexpr int kPlane = 256 * kHS;
     uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -218,7 +252,11 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const float hv = fmaxf(acc[mb][nb][v], 0.f) * acc[mb][nb + 2][v];
-          hs[r * kHS + wn * 64 + nb * 32 + col] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+          const uint32_t hi = f32_to_bf16_rne(hv);
+          hs[r * kHS + wn * 64 + nb * 32 + col] = static_cast<uint16_t>(hi);
+          if constexpr (kHiLo)
+            hs[kPlane + r * kHS + wn * 64 + nb * 32 + col] =
+                static_cast<uint16_t>(f32_to_bf16_rne(hv - __uint_as_float(hi << 16)));
         }
       }
     waitcnt<63, 0>();
@@ -227,9 +265,12 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int piece = i * 256 + tid, r = piece >> 4, p = piece & 15;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(hs + r * kHS + p * 8);
-      if (m0 + r < a.rows_a && n0 + p * 8 < F)
-        *reinterpret_cast<u32x4_t*>(a.h + static_cast<size_t>(m0 + r) * F + n0 + p * 8) = v;
+      if (m0 + r < R && n0 + p * 8 < F) {
+        const size_t o = static_cast<size_t>(m0 + r) * F + n0 + p * 8;
+        *reinterpret_cast<u32x4_t*>(a.h + o) = *reinterpret_cast<const u32x4_t*>(hs + r * kHS + p * 8);
+        if constexpr (kHiLo)
+          *reinterpret_cast<u32x4_t*>(a.h_lo + o) = *reinterpret_cast<const u32x4_t*>(hs + kPlane + r * kHS + p * 8);
+      }
     }
   } else {
     // y in two passes of 128 rows (the waves with wm == pass write theirs),
@@ -257,7 +298,10 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
         const int piece = i * 256 + tid, r = piece >> 6, p = piece & 63;
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ys + r * kYS + p * 4);
         const int row = m0 + pass * 128 + r;
-        if (row < a.rows_a) *reinterpret_cast<f32x4_t*>(dst + static_cast<size_t>(row) * d + n0 + p * 4) = v;
+        if (row < R) {
+          const int out = kGather ? a.rows[row] : row;  // gathering: y row of the list entry's token
+          *reinterpret_cast<f32x4_t*>(dst + static_cast<size_t>(out) * d + n0 + p * 4) = v;
+        }
       }
       waitcnt<63, 0>();
       raw_barrier();  // reads done before the next pass writes
@@ -270,8 +314,11 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
 // 2 (t / 8), 2 (t / 8) + 1 and writes each column's two values as one 32-bit
 // word of the transposed tile, so a 16-byte read there is 8 consecutive rows
 // of one column.
+// With n_rows set, nothing is done when *n_rows < min_rows.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
-                                                        uint16_t* __restrict__ dst, int rows, int cols) {
+                                                        uint16_t* __restrict__ dst, int rows, int cols,
+                                                        const int32_t* n_rows, int min_rows) {
+  if (n_rows != nullptr && *n_rows < min_rows) return;
   constexpr int kTS = 32 + 4;  // 32-bit words per transposed row (16-byte aligned)
   __shared__ __attribute__((aligned(16))) uint32_t tt[64 * kTS];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
@@ -356,7 +403,7 @@ hipError_t launch_dense_ring(const DenseArgs& da, void* ring_ws, hipStream_t s) 
   uint16_t* wdt = static_cast<uint16_t*>(ring_ws);
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ring_ws) + align256(size_t(F) * size_t(d) * 2));
 
-  transpose_kernel<<<dim3(F / 64, d / 64), dim3(256), 0, s>>>(da.Wd, wdt, F, d);
+  transpose_kernel<<<dim3(F / 64, d / 64), dim3(256), 0, s>>>(da.Wd, wdt, F, d, nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -392,6 +439,67 @@ hipError_t launch_dense_ring(const DenseArgs& da, void* ring_ws, hipStream_t s) 
   if (e != hipSuccess || dn.S == 1) return e;
   const int64_t n = int64_t(M) * d;
   add_partials_kernel<<<dim3(static_cast<unsigned>(ceil_div(n / 4, 1024))), dim3(256), 0, s>>>(da.y, part, n, dn.S);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fallback
+int dense_ring_fallback_min_rows(int64_t d) {
+  const int64_t across = d / kRN;  // down tiles across d
+  const int64_t tiles_m = (kCUs + across - 1) / across;
+  return static_cast<int>((tiles_m - 1) * kRM + 1);
+}
+
+bool dense_ring_fallback_possible(int64_t M, int64_t d, int64_t F) {
+  return dense_ring_supports(M, d, F) && M >= dense_ring_fallback_min_rows(d);
+}
+
+size_t dense_ring_fallback_bytes(int64_t d, int64_t F) { return align256(size_t(F) * size_t(d) * 2); }
+
+hipError_t launch_ring_fallback_up(const DenseArgs& da, hipStream_t s) {
+  const int M = da.M, d = da.d, F = da.F;
+  uint16_t* wdt = static_cast<uint16_t*>(da.ring_ws);
+  transpose_kernel<<<dim3(F / 64, d / 64), dim3(256), 0, s>>>(da.Wd, wdt, F, d, da.n_rows, da.ring_min_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RingArgs up{};
+  up.a = da.x;
+  up.b0 = da.Wg;
+  up.b1 = da.WuT;
+  up.rows_a = M;
+  up.rows_b = F;
+  up.K = d;
+  up.S = 1;
+  up.tiles_m = static_cast<int>(ceil_div(M, kRM));
+  up.tiles_n = static_cast<int>(ceil_div(F, 128));
+  up.h = da.h_hi;
+  up.h_lo = da.h_lo;
+  up.rows = da.rows;
+  up.n_rows = da.n_rows;
+  up.min_rows = da.ring_min_rows;
+  ring_kernel<kGatedUp, true, true><<<dim3(up.tiles_m * up.tiles_n), dim3(256), 0, s>>>(up);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fallback_down(const DenseArgs& da, hipStream_t s) {
+  const int M = da.M, d = da.d, F = da.F;
+  const uint16_t* wdt = static_cast<const uint16_t*>(da.ring_ws);
+  RingArgs dn{};
+  dn.a = da.h_hi;
+  dn.a_lo = da.h_lo;
+  dn.kwrap = F;
+  dn.b0 = wdt;
+  dn.b1 = wdt;
+  dn.rows_a = M;
+  dn.rows_b = d;
+  dn.K = 2 * F;
+  dn.S = 1;
+  dn.tiles_m = static_cast<int>(ceil_div(M, kRM));
+  dn.tiles_n = d / kRN;
+  dn.y = da.y;
+  dn.rows = da.rows;
+  dn.n_rows = da.n_rows;
+  dn.min_rows = da.ring_min_rows;
+  ring_kernel<kDown, true, true><<<dim3(dn.tiles_m * dn.tiles_n), dim3(256), 0, s>>>(dn);
   return hipGetLastError();
 }
 

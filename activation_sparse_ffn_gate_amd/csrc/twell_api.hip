@@ -63,6 +63,8 @@ Layout layout(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C)
       L.h_hi = take(m * f * 2);
       L.h_lo = take(m * f * 2);
       L.split = take(twell::kDenseSplitBytes);
+      // a long overflow list runs on the ring kernels, which read Wd^T
+      if (twell::dense_ring_fallback_possible(M, d, F)) L.ring = take(twell::dense_ring_fallback_bytes(d, F));
       break;
     case TWELL_OP_SLICED_UPDOWN:
       L.part = take(twell::sliced_layout(M, F, T, C).total);
@@ -76,6 +78,7 @@ Layout layout(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C)
       L.h_hi = take(m * f * 2);
       L.h_lo = take(m * f * 2);
       L.split = take(twell::kDenseSplitBytes);
+      if (twell::dense_ring_fallback_possible(M, d, F)) L.ring = take(twell::dense_ring_fallback_bytes(d, F));
       break;
     case TWELL_OP_DENSE_FFN:
       L.h_hi = take(m * f * 2);
@@ -85,6 +88,7 @@ Layout layout(int32_t op, int64_t M, int64_t d, int64_t F, int32_t T, int32_t C)
       L.h_hi = take(m * f * 2);
       L.h_lo = take(m * f * 2);
       L.split = take(twell::kDenseSplitBytes);
+      if (twell::dense_ring_fallback_possible(M, d, F)) L.ring = take(twell::dense_ring_fallback_bytes(d, F));
       break;
     default:
       return L;
@@ -227,9 +231,16 @@ int sliced_impl(const uint16_t* x, const uint16_t* WuT, const uint16_t* Wd, cons
   return hip_status(twell::launch_sliced_updown(a, s));
 }
 
+// The fallback's Wd^T region when a list of M rows can reach its ring kernels.
+void* ring_region(void* ws, const Layout& L, int64_t M, int64_t d, int64_t F) {
+  return twell::dense_ring_fallback_possible(M, d, F) ? static_cast<void*>(static_cast<uint8_t*>(ws) + L.ring)
+                                                      : nullptr;
+}
+
 int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
                int64_t M, int64_t d, int64_t F, const int32_t* rows, const int32_t* n_rows,
-               uint16_t* h_hi, uint16_t* h_lo, float* y, float* split_part, bool split_k, hipStream_t s) {
+               uint16_t* h_hi, uint16_t* h_lo, float* y, float* split_part, bool split_k, hipStream_t s,
+               void* ring_ws = nullptr) {
   if (M == 0) return TWELL_OK;
   twell::DenseArgs a;
   a.x = x;
@@ -246,6 +257,8 @@ int dense_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const
   a.y = y;
   a.part = split_part;
   a.split_k = split_k;
+  a.ring_ws = ring_ws;
+  a.ring_min_rows = ring_ws != nullptr ? twell::dense_ring_fallback_min_rows(d) : 0;
   return hip_status(twell::launch_dense(a, s));
 }
 
@@ -670,7 +683,7 @@ int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* 
   const Layout L = layout(TWELL_OP_DENSE_FALLBACK, M, d, F, 0, 0);
   return dense_impl(x, Wg, WuT, Wd, M, d, F, in->ovf_rows, in->n_ovf, at<uint16_t>(workspace, L.h_hi),
                     at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                    true, static_cast<hipStream_t>(stream));
+                    true, static_cast<hipStream_t>(stream), ring_region(workspace, L, M, d, F));
 }
 
 static int ffn_forward_impl(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
@@ -709,7 +722,7 @@ static int ffn_forward_impl(const uint16_t* x, const uint16_t* Wg, const uint16_
     return TWELL_E_HIP;
   const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                                at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                               true, ss->s);
+                               true, ss->s, ring_region(workspace, L, M, d, F));
   // join before anything else can be reported, so the caller's stream never
   // runs ahead of work already on the side stream
   const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
@@ -817,7 +830,7 @@ int twell_ffn_forward_gateup(const uint16_t* x, const uint16_t* Wg, const uint16
     return TWELL_E_HIP;
   const int st_fb = dense_impl(x, Wg, WuT, Wd, M, d, F, p.ovf_rows, p.n_ovf, at<uint16_t>(workspace, L.h_hi),
                                at<uint16_t>(workspace, L.h_lo), y, at<float>(workspace, L.split),
-                               true, ss->s);
+                               true, ss->s, ring_region(workspace, L, M, d, F));
   const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
   st = hidden_down_impl(Wd, &p, M, d, F, T, C, y, s);
   if (!joined || hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return TWELL_E_HIP;

@@ -80,6 +80,11 @@ struct DenseArgs {
   // launch after each product.
   float* part;            // kDenseSplitSlots partial tiles of 64 KB
   bool split_k;           // the gathering kernels may split K
+  // Gathering with a hi/lo hidden only: when the device-side row count
+  // reaches ring_min_rows the ring kernels run the list instead (ring_ws
+  // receives Wd^T); nullptr / 0: the register-staged kernels always do.
+  void* ring_ws = nullptr;
+  int ring_min_rows = 0;
 };
 
 // Partial-tile slots of the split-K fallback: 2 per work item of the gated-up
@@ -184,6 +189,19 @@ bool dense_ring_supports(int64_t M, int64_t d, int64_t F);
 int dense_ring_splits(int64_t M, int64_t d, int64_t F);
 size_t dense_ring_bytes(int64_t M, int64_t d, int64_t F);
 hipError_t launch_dense_ring(const DenseArgs& a, void* ring_ws, hipStream_t s);
+
+// The fallback's ring path, for lists long enough to fill the chip without
+// splitting K (at least dense_ring_fallback_min_rows(d) rows, a count the
+// kernels read on the device): whether a batch of M rows can reach it, the
+// workspace it needs (Wd^T), and its two launch steps, each returning at once
+// for a shorter list (transpose + gated up with a hi/lo hidden; down over
+// K = 2F, the hi and then the lo plane, with y rows scattered to the list's
+// tokens).
+int dense_ring_fallback_min_rows(int64_t d);
+bool dense_ring_fallback_possible(int64_t M, int64_t d, int64_t F);
+size_t dense_ring_fallback_bytes(int64_t d, int64_t F);
+hipError_t launch_ring_fallback_up(const DenseArgs& a, hipStream_t s);
+hipError_t launch_ring_fallback_down(const DenseArgs& a, hipStream_t s);
 hipError_t launch_set_i32(int32_t* p, int32_t v, hipStream_t s);
 
 bool fused_supports_d(int d);

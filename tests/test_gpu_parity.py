@@ -65,6 +65,11 @@ SMALL = {
     # every row overflows (its tiles' z spilled) and is cut over several
     # workgroups
     "split_cut_overflow": scaled(WORKLOADS["sweep_p3pct"], M=24, d=512, F=8192, C=8, mean_nnz=490.0),
+    # The fallback's ring kernels take a list of at least 1793 rows at
+    # d = 8192: every one of 1800 rows overflows here; in the second case
+    # 1459 do, so the ring launches find the list too short and return.
+    "ring_fallback_all": scaled(WORKLOADS["sweep_p11pct"], M=1800, d=8192, F=512, C=4),
+    "ring_fallback_short": scaled(WORKLOADS["sweep_p3pct"], M=1800, d=8192, F=512, C=4),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
