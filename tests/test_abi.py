@@ -307,3 +307,35 @@ def test_static_forward_validation():
     # 256 rows of F = 32768: the z spill alone is 32 MiB
     assert f(FAKE, FAKE, FAKE, FAKE, 256, 1024, 32768, 128, 16, FAKE, None) == E_SCRATCH
     assert f(None, FAKE, FAKE, FAKE, 0, 2048, 8192, 128, 16, None, None) == OK
+
+
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_dense_ring_workspace():
+    """Host sizing of the ring kernels' regions. The dense baseline holds h
+    [M, F] bf16, Wd^T [d, F] bf16 and S - 1 fp32 partial outputs [M, d], where
+    the down product's ceil(M / 256) * (d / 256) output tiles are split
+    S = min(256 / tiles, F / 256) ways below 256 tiles. The forward, the
+    gate-only forward and the standalone fallback gain exactly Wd^T once a
+    batch can hold an overflow list of the ring fallback's length, the first
+    row count whose down tiles reach 256."""
+    def dense_expect(M, d, F):
+        tiles = -(-M // 256) * (d // 256)
+        S = 1 if tiles >= 256 else max(1, min(256 // tiles, (F // 32) // 8))
+        return _a256(M * F * 2) + _a256(F * d * 2) + _a256((S - 1) * M * d * 4)
+
+    for M, d, F in [(4096, 2048, 8192), (1, 512, 2048), (300, 256, 1088), (8192, 2048, 8192),
+                    (16384, 2560, 10240), (300, 8192, 512)]:
+        assert tw.workspace_bytes(tw.OP_DENSE_FFN, M, d, F) == dense_expect(M, d, F), (M, d, F)
+
+    for d, F, first in [(2048, 8192, 7937), (8192, 512, 1793), (2560, 10240, 6401)]:
+        wdt = F * d * 2
+        for op, T, C in [(tw.OP_FFN_FORWARD, 128, 16), (tw.OP_FFN_FORWARD_GATEUP, 128, 16),
+                         (tw.OP_DENSE_FALLBACK, 0, 0)]:
+            w = [tw.workspace_bytes(op, M, d, F, T, C) for M in (first - 2, first - 1, first)]
+            assert w[1] - w[0] < wdt // 2, (op, d)  # one more row: its own few KB
+            assert wdt <= w[2] - w[1] < wdt + wdt // 2, (op, d)  # ... plus Wd^T
+        fb = tw.workspace_bytes(tw.OP_DENSE_FALLBACK, first, d, F)
+        assert fb == 2 * _a256(first * F * 2) + 512 * 64 * 1024 + _a256(wdt)
