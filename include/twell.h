@@ -147,7 +147,13 @@ int twell_sliced_updown(const uint16_t* x, const uint16_t* WuT, const uint16_t* 
  * hi/lo pair. n_ovf is read on the device (no host synchronisation); other rows
  * of y are untouched. When the list is short the K loops are split over more
  * workgroups, and a reduce launch after each product adds their partial
- * tiles in a fixed order (deterministic).
+ * tiles in a fixed order (deterministic). When M is large enough for the list
+ * to fill the device without splitting (256 output tiles of its down product:
+ * 7937 rows at d = 2048), the call also enqueues kernels that take a list of
+ * that length instead (the workspace then also receives Wd^T); which ones do
+ * the work is decided on the device from n_ovf, and the results are the same
+ * bits whichever entry (this one, twell_ffn_forward, the gate-only forward)
+ * ran the fallback.
  * ctrl: >= twell_ctrl_bytes(M) (see above);
  * workspace: >= twell_workspace_bytes(TWELL_OP_DENSE_FALLBACK, ...). */
 int twell_dense_fallback(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT,
