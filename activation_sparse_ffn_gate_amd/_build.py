@@ -21,7 +21,7 @@ LIB_NAME = "libtwell.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["gate_pack.hip", "gate_pack_skinny.hip", "gateup_pack.hip", "fused_updown.hip", "sliced_updown.hip", "dense_ffn.hip", "dense_ring.hip",
+SOURCES = ["gate_pack.hip", "gate_pack_skinny.hip", "fused_updown.hip", "sliced_updown.hip", "dense_ffn.hip", "dense_ring.hip",
            "compact_rows.hip", "backward.hip",
            "twell_api.hip"]
 

@@ -23,8 +23,25 @@
 // range is cut into S splits: split 0 stores into y, split s > 0 into partial
 // s of the workspace, and a last launch adds the partials to y in split
 // order (the sum order is fixed).
+//
+// Gated up with the TwELL packing of h: the gate-only variant of the forward,
+// which the pages do not describe. Their inference path packs the gate output
+// g in the gate GEMM's epilogue and gathers one WuT row and one Wd row per
+// stored unit (Telegram post on TwELL at tgviewer.app, part "Инференс";
+// aimodeling.com summary, paragraph 3). When more units are active the per-
+// unit up gathers cost more than a dense up product, so here the up product
+// is dense, from the same x tile as the gate, and only the down product
+// gathers (one Wd row per stored unit). The active set stays the gate's: a
+// unit with z > 0 is stored even where h is zero or negative (the gate decides
+// which units are live: Tencent Cloud article, section 1), and z is computed
+// exactly as the gate kernel computes it, so counts, slots, tile-local indices
+// and the overflow set are those of twell_gate_pack; only the stored value,
+// h = ReLU(z) u in fp32, differs. The packing is done from the registers with
+// ballots and per-token counts (the two waves of a 128-unit tile add theirs
+// through LDS).
 #include <algorithm>
 
+#include "gate_overflow.hpp"
 #include "twell_device.hpp"
 #include "twell_internal.hpp"
 
@@ -42,7 +59,7 @@ constexpr int kRDma = 8;          // global_load_lds per thread per stage (4 for
 constexpr int kMinChunks = 8;     // K chunks per split at least (the pipeline's prologue and drain)
 constexpr int kCUs = 256;
 
-enum RingMode { kGatedUp = 0, kDown = 1 };
+enum RingMode { kGatedUp = 0, kDown = 1, kGatedUpPack = 2 };
 
 struct RingArgs {
   const uint16_t* a;   // A rows [rows_a, K] (hi/lo down: the hi plane, [rows_a, kwrap])
@@ -62,6 +79,9 @@ struct RingArgs {
   const int32_t* rows;
   const int32_t* n_rows;
   int min_rows;
+  // gated up with the TwELL packing of h (the gate-only variant): outputs,
+  // control block, T and C as for the gate kernel
+  GateArgs g;
 };
 
 // kGather: rows come from a device-side list (S = 1, tiles_m from its
@@ -75,7 +95,8 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  constexpr int kTileN = kMode == kGatedUp ? 128 : 256;  // output columns per tile
+  constexpr bool kGU = kMode != kDown;  // the B rows interleave Wg and WuT
+  constexpr int kTileN = kGU ? 128 : 256;  // output columns per tile
 
   int R = a.rows_a, tiles_m = a.tiles_m;
   if constexpr (kGather) {
@@ -117,15 +138,15 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
     const int row = (w * 4 + i) * 16 + (lane >> 2);
     const uint32_t lp = static_cast<uint32_t>((lane & 3) ^ lds_swz(row)) * 16u;
     int arow = min(m0 + row, R - 1);
-    if constexpr (kGather && kMode == kGatedUp) arow = a.rows[arow];  // x row of list entry arow
+    if constexpr (kGather && kGU) arow = a.rows[arow];  // x row of list entry arow
     oa[i] = static_cast<uint32_t>(arow) * row_bytes + lp;
     // gated up: B rows 64g .. 64g+63 are Wg (g even) or WuT (g odd) rows of
     // units n0 + 64 (g / 2) + 0..63, and wave w's blocks all lie in g = w
-    const int brow = kMode == kGatedUp ? n0 + (w >> 1) * 64 + i * 16 + (lane >> 2) : n0 + row;
+    const int brow = kGU ? n0 + (w >> 1) * 64 + i * 16 + (lane >> 2) : n0 + row;
     ob[i] = static_cast<uint32_t>(min(brow, a.rows_b - 1)) * row_bytes + lp;
   }
   const char* abase = reinterpret_cast<const char*>(a.a) + static_cast<size_t>(c0) * kRK * 2;
-  const char* bbase = reinterpret_cast<const char*>((kMode == kGatedUp && (w & 1)) ? a.b1 : a.b0) +
+  const char* bbase = reinterpret_cast<const char*>((kGU && (w & 1)) ? a.b1 : a.b0) +
                       static_cast<size_t>(c0) * kRK * 2;
   auto dma = [&](int j, int buf, int k0) {
     uint8_t* st = smem + buf * kRStageBytes + w * 4 * 1024;
@@ -272,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
           *reinterpret_cast<u32x4_t*>(a.h_lo + o) = *reinterpret_cast<const u32x4_t*>(hs + kPlane + r * kHS + p * 8);
       }
     }
-  } else {
+  } else if constexpr (kMode == kDown) {
     // y in two passes of 128 rows (the waves with wm == pass write theirs),
     // fp32 rows of 256 (+8 padding) columns
     constexpr int kYS = 256 + 8;
@@ -306,6 +327,116 @@ __global__ __launch_bounds__(256, 1) void ring_kernel(RingArgs a) {
       waitcnt<63, 0>();
       raw_barrier();  // reads done before the next pass writes
     }
+  } else {
+    // The gate-only variant's packing, from the registers: z decides which
+    // units are stored (the gate's own active set, z computed as the gate
+    // kernel computes it), h = ReLU(z) u is the stored value. Wave (wm, wn)
+    // holds 128 tokens x 64 units; with T = 128 the wave pair wn = 0, 1 is one
+    // tile (wn = 0 first), with T = 64 each wave's units are a tile.
+    const GateArgs& g = a.g;
+    const int F = a.rows_b;
+    const int wrow0 = m0 + wm * 128, ucol0 = n0 + wn * 64;
+    // rows and units past the matrix never count
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int c = ucol0 + nb * 32 + col;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wrow0 + mb * 32 + acc_row(v, half);
+          const float z = (row < R && c < F) ? acc[mb][nb][v] : 0.f;
+          acc[mb][nb][v] = z;
+          acc[mb][nb + 2][v] = fmaxf(z, 0.f) * acc[mb][nb + 2][v];
+        }
+      }
+    if (g.z_debug != nullptr) {  // bit-exact checks: every z and h of the tile
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wrow0 + mb * 32 + acc_row(v, half), c = ucol0 + nb * 32 + col;
+            if (row < R && c < F) {
+              g.z_debug[static_cast<size_t>(row) * F + c] = acc[mb][nb][v];
+              g.h_debug[static_cast<size_t>(row) * F + c] = acc[mb][nb + 2][v];
+            }
+          }
+    }
+    // Each token's count in this wave's 64 units: lane t holds token t (cw0)
+    // and token 64 + t (cw1).
+    int cw0 = 0, cw1 = 0;
+    static_for<0, 64>([&](auto I) {
+      constexpr int mb = decltype(I)::value / 16, v = decltype(I)::value % 16;
+      constexpr int t0 = (mb & 1) * 32 + acc_row(v, 0), t1 = (mb & 1) * 32 + acc_row(v, 1);
+      const uint64_t b0 = __ballot(acc[mb][0][v] > 0.f), b1 = __ballot(acc[mb][1][v] > 0.f);
+      const int lo = __popc(static_cast<uint32_t>(b0)) + __popc(static_cast<uint32_t>(b1));
+      const int hi = __popc(static_cast<uint32_t>(b0 >> 32)) + __popc(static_cast<uint32_t>(b1 >> 32));
+      if constexpr (mb < 2) {
+        cw0 = writelane<t0>(cw0, lo);
+        cw0 = writelane<t1>(cw0, hi);
+      } else {
+        cw1 = writelane<t0>(cw1, lo);
+        cw1 = writelane<t1>(cw1, hi);
+      }
+    });
+    int* s_cnt = reinterpret_cast<int*>(smem);  // [wm][wn][128 tokens]
+    int* s_flag = s_cnt + 2 * 2 * 128;
+    s_cnt[(wm * 2 + wn) * 128 + lane] = cw0;
+    s_cnt[(wm * 2 + wn) * 128 + 64 + lane] = cw1;
+    __syncthreads();
+    const bool pair = g.T == 128;
+    const int* c0 = s_cnt + (wm * 2) * 128;   // the wave pair's wn = 0 counts
+    const int* c1 = c0 + 128;                 // ... and wn = 1
+    const int pre0 = (pair && wn == 1) ? c0[lane] : 0, pre1 = (pair && wn == 1) ? c0[64 + lane] : 0;
+    const int tot0 = pair ? c0[lane] + c1[lane] : cw0, tot1 = pair ? c0[64 + lane] + c1[64 + lane] : cw1;
+    const int nT = F / g.T;
+    const int tile = pair ? n0 / g.T : ucol0 / g.T;
+    const int C = g.C;
+    int appended = 0;
+    if (tile < nT) {
+      const uint32_t row_slots = static_cast<uint32_t>(nT * C);
+      const int ubase = pair ? wn * 64 : 0;  // tile-local index of the wave's first unit
+      static_for<0, 64>([&](auto I) {
+        constexpr int mb = decltype(I)::value / 16, v = decltype(I)::value % 16;
+        constexpr int t_lo = (mb & 1) * 32 + acc_row(v, 0), t_hi = (mb & 1) * 32 + acc_row(v, 1);
+        const uint64_t b0 = __ballot(acc[mb][0][v] > 0.f), b1 = __ballot(acc[mb][1][v] > 0.f);
+        if ((b0 | b1) == 0) return;
+        const int pre = mb < 2 ? pre0 : pre1;
+        const uint32_t p = half ? static_cast<uint32_t>(__builtin_amdgcn_readlane(pre, t_hi))
+                                : static_cast<uint32_t>(__builtin_amdgcn_readlane(pre, t_lo));
+        const uint32_t row = static_cast<uint32_t>(wrow0 + mb * 32 + acc_row(v, half));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint64_t bq = nb ? b1 : b0;
+          if (bq == 0) continue;
+          // slot: active units left of this one in the token's tile
+          uint32_t rank = half ? __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32), 0u)
+                               : __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bq), 0u);
+          if (nb == 1) rank += half ? __popc(static_cast<uint32_t>(b0 >> 32)) : __popc(static_cast<uint32_t>(b0));
+          const uint32_t slot = rank + p;
+          if (acc[mb][nb][v] > 0.f && slot < static_cast<uint32_t>(C)) {
+            const uint32_t at = row * row_slots + static_cast<uint32_t>(tile * C) + slot;
+            store_at(g.vals, at * 4u, acc[mb][nb + 2][v]);
+            store_at(g.idx, at, static_cast<uint8_t>(ubase + nb * 32 + col));
+          }
+        }
+      });
+      // counts and overflow membership: the tile's first wave, lane t =
+      // tokens t and 64 + t of the wave's rows
+      if (!pair || wn == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = wrow0 + hh * 64 + lane, tot = hh ? tot1 : tot0;
+          if (row < R) {
+            g.counts[static_cast<size_t>(row) * nT + tile] = static_cast<uint16_t>(tot);
+            if (tot > C) appended |= overflow_append(g, row);
+          }
+        }
+      }
+    }
+    overflow_finalize(g, appended, s_flag);
   }
 }
 
@@ -500,6 +631,25 @@ hipError_t launch_ring_fallback_down(const DenseArgs& da, hipStream_t s) {
   dn.n_rows = da.n_rows;
   dn.min_rows = da.ring_min_rows;
   ring_kernel<kDown, true, true><<<dim3(dn.tiles_m * dn.tiles_n), dim3(256), 0, s>>>(dn);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- gate-only variant
+hipError_t launch_gateup_pack(const GateArgs& a, hipStream_t s) {
+  if (a.WuT == nullptr || (a.z_debug == nullptr) != (a.h_debug == nullptr)) return hipErrorInvalidValue;
+  if (a.d % kRN != 0 || a.d / kRK < kMinChunks) return hipErrorInvalidValue;
+  RingArgs up{};
+  up.a = a.x;
+  up.b0 = a.Wg;
+  up.b1 = a.WuT;
+  up.rows_a = a.M;
+  up.rows_b = a.F;
+  up.K = a.d;
+  up.S = 1;
+  up.tiles_m = static_cast<int>(ceil_div(a.M, kRM));
+  up.tiles_n = static_cast<int>(ceil_div(a.F, 128));
+  up.g = a;
+  ring_kernel<kGatedUpPack><<<dim3(up.tiles_m * up.tiles_n), dim3(256), 0, s>>>(up);
   return hipGetLastError();
 }
 
