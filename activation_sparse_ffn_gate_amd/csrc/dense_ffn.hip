@@ -1,5 +1,7 @@
-// Dense gated FFN on MFMA, for gfx950: the dense baseline and the dense
-// fallback of overflow rows.
+// Dense gated FFN on MFMA with register-staged 128 x 128 tiles, for gfx950:
+// the dense fallback of overflow rows (every list but those long enough for
+// the ring kernels of dense_ring.hip), and the dense baseline for shapes whose
+// operands exceed the ring kernels' 32-bit offsets.
 //
 // Kernel 1 (gated up): for a block of rows, z = x Wg^T and u = x WuT^T share
 // one A tile; the epilogue forms h = ReLU(z) * u and stores it as bf16, or as

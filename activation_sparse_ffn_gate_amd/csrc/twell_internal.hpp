@@ -180,6 +180,8 @@ hipError_t launch_fused_updown(const FusedArgs& a, hipStream_t s);
 // epilogue (vals hold h), then the down product from that packing.
 hipError_t launch_gateup_pack(const GateArgs& a, hipStream_t s);
 hipError_t launch_hidden_down(const SlicedArgs& a, hipStream_t s);
+// Register-staged dense kernels: gathering (rows != nullptr) for the
+// fallback, which also enqueues the ring kernels when ring_ws is set.
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 
 // Dense baseline on the gate kernel's LDS-DMA ring (rows 0..M-1, bf16 h):
