@@ -1,6 +1,7 @@
 // Dense gated FFN on the gate kernel's LDS-DMA ring, for gfx950: the dense
 // baseline (the dense matmuls the pages compare against: tgviewer.app
-// Telegram post, paragraph after "Обучение").
+// Telegram post, paragraph after "Обучение"), the dense fallback of long
+// overflow lists, and the gate-only variant's dense products.
 //
 // Both products are run as C = A B^T with A and B row-major, K contiguous,
 // which is the form the gate kernel's pipeline streams: 256 x 256 output
@@ -23,6 +24,15 @@
 // range is cut into S splits: split 0 stores into y, split s > 0 into partial
 // s of the workspace, and a last launch adds the partials to y in split
 // order (the sum order is fixed).
+//
+// Fallback of long overflow lists (rows that do not fit the sparse block go to
+// a dense path: Telegram post, part "Обучение"; Tencent Cloud article,
+// section 3): the same two products over the list's rows, read on the device
+// (gated up: A rows are the listed tokens' x rows; down: y rows are scattered
+// to them), with the hidden kept as a bf16 hi/lo pair and the down product run
+// over K = 2F, the hi plane and then the lo plane against the same Wd^T.
+// These launches return at once for a list too short to fill the chip
+// without splitting K; the register-staged kernels of dense_ffn.hip take it.
 //
 // Gated up with the TwELL packing of h: the gate-only variant of the forward,
 // which the pages do not describe. Their inference path packs the gate output
