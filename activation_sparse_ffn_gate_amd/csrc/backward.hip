@@ -362,97 +362,177 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
           make_float4(acc[ch][k], acc[ch][k + 1], acc[ch][k + 2], acc[ch][k + 3]);
 }
 
-// Reserve rows: one workgroup of kResWaves waves per reserve slot (long rows:
-// many units' gathers in flight at once). The dense
-// g row is compacted into an ascending (unit, g) list in LDS (each wave counts
-// a contiguous column range, a prefix over the waves places them); each wave
-// takes a contiguous run of the list; the waves' dx rows are added in wave
-// order through LDS (kRedCols columns at a time, reusing the list's space).
-// kResWaves waves: 16 while a wave's rows fit in 128 registers (d <= 2048),
-// else 8; the reduction takes kRedCols = 32768 / kResWaves columns a pass.
+// Reserve rows. A row's active units are cut into runs of about kResRunMin
+// (at most kResMaxRuns runs), and a persistent grid of workgroups of
+// kResWaves waves walks the (row, run) work items: a few long rows then spread
+// over the chip instead of keeping one workgroup busy each, while a short row
+// stays one item. reserve_plan_kernel numbers the items (the first item of
+// each row, a prefix over the rows). An item compacts its row's dense g into
+// the ascending (unit, g) list (each wave counts a contiguous column range, a
+// prefix over the waves places them) but keeps only its run in LDS; each wave
+// takes a contiguous part of the run; the waves' dx rows are added in wave
+// order through LDS (kRedCols columns at a time) into the run's partial dx
+// row, and reserve_sum_kernel adds a row's runs in run order. kResWaves: 16
+// while a wave's rows fit in 128 registers (d <= 2048), else 8.
+constexpr int kResRunMin = 128;  // units per run (the last runs of a row may hold more)
+constexpr int kResListCap = (kBackwardMaxF + kResMaxRuns - 1) / kResMaxRuns;  // a run's entries at most
+constexpr int kResLdsBytes = 32768;  // the run's list, then the reduction
+static_assert(kResListCap * 8 <= kResLdsBytes, "a run's list fits");
+
+__device__ __forceinline__ int reserve_runs(int n) {
+  return min(kResMaxRuns, max(1, (n + kResRunMin - 1) / kResRunMin));
+}
+
+// One workgroup: res_prefix[s] = first item of reserve row s, res_prefix[n_res]
+// = the number of items.
+__global__ __launch_bounds__(1024) void reserve_plan_kernel(BackwardArgs a) {
+  __shared__ int s_sum[1024];
+  const int n_res = min(*a.n_res, a.R);
+  const int t = threadIdx.x;
+  const int per = (n_res + 1023) / 1024;
+  const int lo = min(n_res, t * per), hi = min(n_res, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += reserve_runs(a.h_count[a.res_rows[i]]);
+  s_sum[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan over the threads' sums
+    const int v = t >= off ? s_sum[t - off] : 0;
+    __syncthreads();
+    s_sum[t] += v;
+    __syncthreads();
+  }
+  int run = s_sum[t] - sum;
+  for (int i = lo; i < hi; ++i) {
+    a.res_prefix[i] = run;
+    run += reserve_runs(a.h_count[a.res_rows[i]]);
+  }
+  if (t == 1023) a.res_prefix[n_res] = s_sum[1023];
+}
+
 template <int VEC, int NCH, int UNROLL, int kResWaves>
 __global__ __launch_bounds__(64 * kResWaves) void reserve_backward_kernel(BackwardArgs a) {
-  constexpr int kRedCols = 32768 / kResWaves;
-  static_assert(kResWaves * kRedCols * 4 <= kBackwardMaxF * 8, "the reduction fits in the list's space");
+  constexpr int kRedCols = kResLdsBytes / 4 / kResWaves;
   using LoadT = typename Vec<VEC>::T;
   constexpr int kChunk = 64 * VEC;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kBackwardMaxF * 8];
+  static_assert(kRedCols % kChunk == 0, "a chunk's columns lie in one reduction pass");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kResLdsBytes];
   __shared__ int s_cnt[kResWaves];
   int* lj = reinterpret_cast<int*>(smem);
-  float* lg = reinterpret_cast<float*>(smem + kBackwardMaxF * 4);
+  float* lg = reinterpret_cast<float*>(smem + kResListCap * 4);
   float* red = reinterpret_cast<float*>(smem);  // [kResWaves][kRedCols], after the list is done
 
-  const int slot = blockIdx.x;
-  if (slot >= min(*a.n_res, a.R)) return;
+  const int n_res = min(*a.n_res, a.R);
+  if (n_res <= 0) return;
+  const int items = a.res_prefix[n_res];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int r = a.res_rows[slot];
-  const int n = a.h_count[r];
-  const int64_t e0 = a.row_off[r];
-  const float* dense = a.res_vals + static_cast<size_t>(slot) * a.F;
-
-  // Compaction: wave w scans columns [w span, (w + 1) span).
-  const int span = ((a.F + 64 * kResWaves - 1) / (64 * kResWaves)) * 64;
-  const int c_lo = min(a.F, w * span), c_hi = min(a.F, c_lo + span);
-  int cnt = 0;
-  for (int c = c_lo; c < c_hi; c += 64) {
-    const int j = c + lane;
-    cnt += __popcll(__ballot(j < c_hi && dense[j] > 0.f));
-  }
-  if (lane == 0) s_cnt[w] = cnt;
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int v = 0; v < kResWaves; ++v) {
-    base += v < w ? s_cnt[v] : 0;
-    total += s_cnt[v];
-  }
-  for (int c = c_lo; c < c_hi; c += 64) {
-    const int j = c + lane;
-    const float g = j < c_hi ? dense[j] : 0.f;
-    const uint64_t bal = __ballot(g > 0.f);
-    if (g > 0.f) {
-      const int at = base + static_cast<int>(mask_rank(bal));
-      lj[at] = j;
-      lg[at] = g;
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    // the item's row: the last s with res_prefix[s] <= item
+    int lo = 0, hi = n_res - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.res_prefix[mid] <= item) lo = mid;
+      else hi = mid - 1;
     }
-    base += __popcll(bal);
-  }
-  __syncthreads();
+    const int slot = lo;
+    const int run = item - a.res_prefix[slot];
+    const int r = a.res_rows[slot];
+    const int n = a.h_count[r];
+    const int runs = reserve_runs(n);
+    const int64_t e0 = a.row_off[r];
+    const float* dense = a.res_vals + static_cast<size_t>(slot) * a.F;
 
-  const int m = min(total, n);
-  LoadT xv[NCH], dyv[NCH];
-  load_row<VEC, NCH>(a.x, a.d, r, xv);
-  load_row<VEC, NCH>(a.dy, a.d, r, dyv);
-  float acc[NCH][VEC];
+    // Compaction: wave w scans columns [w span, (w + 1) span).
+    const int span = ((a.F + 64 * kResWaves - 1) / (64 * kResWaves)) * 64;
+    const int c_lo = min(a.F, w * span), c_hi = min(a.F, c_lo + span);
+    int cnt = 0;
+    for (int c = c_lo; c < c_hi; c += 64) {
+      const int j = c + lane;
+      cnt += __popcll(__ballot(j < c_hi && dense[j] > 0.f));
+    }
+    if (lane == 0) s_cnt[w] = cnt;
+    __syncthreads();
+    int base = 0, total = 0;
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) acc[ch][k] = 0.f;
-  const int per = (m + kResWaves - 1) / kResWaves;
-  const int k_lo = min(m, w * per), k_hi = min(m, k_lo + per);
-  if (k_hi > k_lo) process_entries<VEC, NCH, UNROLL>(a, r, lj + k_lo, lg + k_lo, k_hi - k_lo, e0 + k_lo, xv, dyv, acc);
-  if (w == 0 && m < n) mark_unused(a, e0 + m, e0 + n);
-  __syncthreads();  // the list is no longer read
-
-  float* dxr = a.dx + static_cast<size_t>(r) * a.d;
-  for (int col0 = 0; col0 < a.d; col0 += kRedCols) {
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int c = ch * kChunk + lane * VEC;  // this lane's first column of chunk ch
-      if (ch * kChunk >= col0 && ch * kChunk < col0 + kRedCols) {  // uniform
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) red[w * kRedCols + (c - col0) + k] = acc[ch][k];
+    for (int v = 0; v < kResWaves; ++v) {
+      base += v < w ? s_cnt[v] : 0;
+      total += s_cnt[v];
+    }
+    const int m = min(total, n);
+    // this item's run of the list: entries [k_run, k_run + m_run)
+    const int k_run = static_cast<int>(static_cast<int64_t>(m) * run / runs);
+    const int m_run = static_cast<int>(static_cast<int64_t>(m) * (run + 1) / runs) - k_run;
+    for (int c = c_lo; c < c_hi; c += 64) {
+      const int j = c + lane;
+      const float g = j < c_hi ? dense[j] : 0.f;
+      const uint64_t bal = __ballot(g > 0.f);
+      if (g > 0.f) {
+        const int at = base + static_cast<int>(mask_rank(bal)) - k_run;
+        if (at >= 0 && at < m_run) {
+          lj[at] = j;
+          lg[at] = g;
+        }
       }
+      base += __popcll(bal);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < kRedCols && col0 + c < a.d; c += 64 * kResWaves) {
-      float sum = 0.f;
+
+    LoadT xv[NCH], dyv[NCH];
+    load_row<VEC, NCH>(a.x, a.d, r, xv);
+    load_row<VEC, NCH>(a.dy, a.d, r, dyv);
+    float acc[NCH][VEC];
 #pragma unroll
-      for (int v = 0; v < kResWaves; ++v) sum += red[v * kRedCols + c];
-      dxr[col0 + c] = sum;
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[ch][k] = 0.f;
+    const int per = (m_run + kResWaves - 1) / kResWaves;
+    const int k_lo = min(m_run, w * per), k_hi = min(m_run, k_lo + per);
+    if (k_hi > k_lo)
+      process_entries<VEC, NCH, UNROLL>(a, r, lj + k_lo, lg + k_lo, k_hi - k_lo, e0 + k_run + k_lo, xv, dyv, acc);
+    if (run == 0 && w == 0 && m < n) mark_unused(a, e0 + m, e0 + n);
+    __syncthreads();  // the list is no longer read
+
+    float* prow = a.res_part + (static_cast<size_t>(slot) * kResMaxRuns + run) * a.d;
+    for (int col0 = 0; col0 < a.d; col0 += kRedCols) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const int c = ch * kChunk + lane * VEC;  // this lane's first column of chunk ch
+        if (ch * kChunk >= col0 && ch * kChunk < col0 + kRedCols) {  // uniform
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) red[w * kRedCols + (c - col0) + k] = acc[ch][k];
+        }
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < kRedCols && col0 + c < a.d; c += 64 * kResWaves) {
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < kResWaves; ++v) sum += red[v * kRedCols + c];
+        prow[col0 + c] = sum;
+      }
+      __syncthreads();  // before the next pass, or the next item's list, writes
     }
-    __syncthreads();
+  }
+}
+
+// dx of each reserve row: its runs' partial rows added in run order.
+__global__ __launch_bounds__(256) void reserve_sum_kernel(BackwardArgs a) {
+  const int n_res = min(*a.n_res, a.R);
+  for (int slot = blockIdx.x; slot < n_res; slot += gridDim.x) {
+    const int runs = a.res_prefix[slot + 1] - a.res_prefix[slot];
+    const int r = a.res_rows[slot];
+    const float* p0 = a.res_part + static_cast<size_t>(slot) * kResMaxRuns * a.d;
+    float* dxr = a.dx + static_cast<size_t>(r) * a.d;
+    for (int c = threadIdx.x * 4; c < a.d; c += 256 * 4) {
+      float4 s = *reinterpret_cast<const float4*>(p0 + c);
+      for (int q = 1; q < runs; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(p0 + static_cast<size_t>(q) * a.d + c);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+      *reinterpret_cast<float4*>(dxr + c) = s;
+    }
   }
 }
 
@@ -544,8 +624,14 @@ hipError_t launch_rows(const BackwardArgs& a, hipStream_t s) {
   if (e != hipSuccess || a.R == 0) return e;
   // 16 waves of a workgroup leave 128 registers a wave: one unit at a time
   constexpr int kWaves = VEC * NCH <= 32 ? 16 : 8;
+  reserve_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // persistent: one workgroup per CU at most (16 waves of 128 registers)
+  const int grid = static_cast<int>(std::min<int64_t>(256, int64_t(a.R) * kResMaxRuns));
   reserve_backward_kernel<VEC, NCH, kWaves == 16 ? 1 : row_unroll<NCH>(), kWaves>
-      <<<dim3(a.R), dim3(64 * kWaves), 0, s>>>(a);
+      <<<dim3(grid), dim3(64 * kWaves), 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  reserve_sum_kernel<<<dim3(static_cast<unsigned>(std::min<int64_t>(a.R, 1024))), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int VEC, int NCH>

@@ -459,7 +459,7 @@ int side_stream_locked(int dev, SideStream** out) {
 // unit-major order.
 struct BwdLayout {
   size_t row_off = 0, hist = 0, unit_tot = 0, unit_base = 0, e_unit = 0, e_row = 0, perm = 0;
-  size_t e_h = 0, e_dz = 0, e_du = 0, total = 0;
+  size_t e_h = 0, e_dz = 0, e_du = 0, res_prefix = 0, res_part = 0, total = 0;
   int64_t E_max = 0;
 };
 
@@ -471,7 +471,7 @@ int check_bwd(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
   return TWELL_OK;
 }
 
-BwdLayout bwd_layout(int64_t M, int64_t F, int32_t K, int64_t R) {
+BwdLayout bwd_layout(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
   BwdLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -492,6 +492,8 @@ BwdLayout bwd_layout(int64_t M, int64_t F, int32_t K, int64_t R) {
   L.e_h = take(e4);
   L.e_dz = take(e4);
   L.e_du = take(e4);
+  L.res_prefix = take(size_t(R + 1) * 4);
+  L.res_part = take(size_t(R) * twell::kResMaxRuns * size_t(d) * 4);
   L.total = off;
   return L;
 }
@@ -580,7 +582,7 @@ int twell_gate_pack_spill(const uint16_t* x, const uint16_t* Wg, int64_t M, int6
 
 size_t twell_backward_workspace_bytes(int64_t M, int64_t d, int64_t F, int32_t K, int64_t R) {
   if (check_bwd(M, d, F, K, R) != TWELL_OK) return 0;
-  return bwd_layout(M, F, K, R).total;
+  return bwd_layout(M, d, F, K, R).total;
 }
 
 int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* WuT, const uint16_t* Wd,
@@ -592,7 +594,7 @@ int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu
   if (R != 0 && (!hy->res_vals || !hy->res_rows)) return TWELL_E_INVALID_ARG;
   int st = check_bwd(M, d, F, K, R);
   if (st != TWELL_OK) return st;
-  const BwdLayout L = bwd_layout(M, F, K, R);
+  const BwdLayout L = bwd_layout(M, d, F, K, R);
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || ws_bytes < L.total)
     return TWELL_E_WORKSPACE;
   twell::BackwardArgs a;
@@ -627,6 +629,8 @@ int twell_ffn_backward(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu
   a.e_h = at<float>(workspace, L.e_h);
   a.e_dz = at<float>(workspace, L.e_dz);
   a.e_du = at<float>(workspace, L.e_du);
+  a.res_prefix = at<int32_t>(workspace, L.res_prefix);
+  a.res_part = at<float>(workspace, L.res_part);
   return hip_status(twell::launch_backward(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -165,8 +165,11 @@ struct BackwardArgs {
   int32_t* unit_base;  // [F + 1]
   int32_t *e_unit, *e_row, *perm;  // [E_max]
   float *e_h, *e_dz, *e_du;        // [E_max]
+  int32_t* res_prefix;  // [R + 1]: first work item of each reserve row (its runs follow)
+  float* res_part;      // [R, kResMaxRuns, d]: each run's partial dx row
 };
 constexpr int kBackwardMaxF = 16384;  // the entry placement keeps one counter per unit in LDS (64 KB)
+constexpr int kResMaxRuns = 16;       // runs a reserve row's units are cut into at most
 bool backward_supports_d(int d);
 int backward_sort_blocks(int64_t M);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
