@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * kRowsPerWG) void row_backward_kernel(BackwardA
 // order through LDS (kRedCols columns at a time) into the run's partial dx
 // row, and reserve_sum_kernel adds a row's runs in run order. kResWaves: 16
 // while a wave's rows fit in 128 registers (d <= 2048), else 8.
-constexpr int kResRunMin = 128;  // units per run (the last runs of a row may hold more)
+constexpr int kResRunMin = 192;  // units per run (the last runs of a row may hold more)
 constexpr int kResListCap = (kBackwardMaxF + kResMaxRuns - 1) / kResMaxRuns;  // a run's entries at most
 constexpr int kResLdsBytes = 32768;  // the run's list, then the reduction
 static_assert(kResListCap * 8 <= kResLdsBytes, "a run's list fits");
@@ -446,7 +446,8 @@ __global__ __launch_bounds__(64 * kResWaves) void reserve_backward_kernel(Backwa
     const int span = ((a.F + 64 * kResWaves - 1) / (64 * kResWaves)) * 64;
     const int c_lo = min(a.F, w * span), c_hi = min(a.F, c_lo + span);
     int cnt = 0;
-    for (int c = c_lo; c < c_hi; c += 64) {
+#pragma unroll 4
+    for (int c = c_lo; c < c_hi; c += 64) {  // four columns' loads in flight
       const int j = c + lane;
       cnt += __popcll(__ballot(j < c_hi && dense[j] > 0.f));
     }
@@ -462,7 +463,9 @@ __global__ __launch_bounds__(64 * kResWaves) void reserve_backward_kernel(Backwa
     // this item's run of the list: entries [k_run, k_run + m_run)
     const int k_run = static_cast<int>(static_cast<int64_t>(m) * run / runs);
     const int m_run = static_cast<int>(static_cast<int64_t>(m) * (run + 1) / runs) - k_run;
-    for (int c = c_lo; c < c_hi; c += 64) {
+    // only waves whose columns hold some of the run's entries place any
+    const bool mine = base < k_run + m_run && base + cnt > k_run;
+    for (int c = c_lo; mine && c < c_hi; c += 64) {
       const int j = c + lane;
       const float g = j < c_hi ? dense[j] : 0.f;
       const uint64_t bal = __ballot(g > 0.f);
