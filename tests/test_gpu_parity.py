@@ -72,6 +72,8 @@ SMALL = {
     "ring_fallback_short": scaled(WORKLOADS["sweep_p3pct"], M=1800, d=8192, F=512, C=4),
     # the same with F % 128 == 64: the last gated-up tile holds 64 units
     "ring_fallback_f576": scaled(WORKLOADS["sweep_p11pct"], M=1800, d=8192, F=576, T=64, C=4),
+    # d = 4096: the ring path from 3841 rows, 16 down tiles across
+    "ring_fallback_d4096": scaled(WORKLOADS["sweep_p11pct"], M=3900, d=4096, F=512, C=4),
 }
 FULL = ["ffn1p5b", "ffn1p5b_heavytail", "ffn2b_zipf"] + [
     k for k in WORKLOADS if k.startswith(("sweep_", "decode_"))
